@@ -1,0 +1,62 @@
+"""Plants plausible mistakes in a copy of the oracle, on the CPU, and checks that
+the oracle's pins (not the scalar brute force, which restates the formulas)
+catch every one of them."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTATIONS = {
+    "no_bias_correction_m": ('m_hat = _chk32(m1 / sc["bias_correction1"])', 'm_hat = _chk32(m1 / F32(1))'),
+    "eps_inside_sqrt": ('denom = _chk32(np.sqrt(v_hat) + sc["eps"])', 'denom = _chk32(np.sqrt(v_hat + sc["eps"]))'),
+    "beta2_in_first_moment": ('m1 = _chk32(_chk32(sc["beta1"] * m) + _chk32(sc["one_minus_beta1"] * g))',
+                              'm1 = _chk32(_chk32(sc["beta2"] * m) + _chk32(sc["one_minus_beta2"] * g))'),
+    "wrong_decay_factor": ('m1 = _chk32(_chk32(sc["beta1"] * m)', 'm1 = _chk32(_chk32(sc["beta2"] * m)'),
+    "weight_decay_dropped": ('u = _chk32(u + _chk32(sc["weight_decay"] * p))', 'u = u'),
+    "update_sign": ('p1 = _chk32(p - _chk32(sc["lr"] * u))', 'p1 = _chk32(p + _chk32(sc["lr"] * u))'),
+    "bias_correction1_exponent": ("math.pow(float(b1), step)", "math.pow(float(b1), step + 1)"),
+    "bias_correction2_exponent": ("math.pow(float(b2), step)", "math.pow(float(b2), step - 1 if step > 1 else 1)"),
+    "second_moment_not_squared": ("gg = _chk32(g * g)", "gg = _chk32(np.abs(g))"),
+    "last_rank_dropped": ("for r in range(1, len(rank_grads)):", "for r in range(1, len(rank_grads) - 1):"),
+    "owner_slice_shifted": ("    lo, hi = shard_bounds(rank_grads[0].size, n_shards, k)\n",
+                            "    lo, hi = shard_bounds(rank_grads[0].size, n_shards, k)\n"
+                            "    lo, hi = (lo + 1, hi + 1) if hi < rank_grads[0].size else (lo, hi)\n"),
+    "weight_paired_with_wrong_rank": ("term = _chk32(weights[r] * bf16_to_f32(rank_grads[r]))",
+                                      "term = _chk32(weights[(r + 1) % len(rank_grads)] * bf16_to_f32(rank_grads[r]))"),
+    "bf16_ties_away": ("take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & lo_odd)", "take_hi = (d_hi <= d_lo)"),
+    "bf16_truncates": ("take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & lo_odd)", "take_hi = d_hi < 0"),
+    "bf16_widen_shift": ("<< U32(16)).view(F32)", "<< U32(15)).view(F32)"),
+    "count_weights_off": ("total = float(sum(counts))", "total = float(sum(counts) + 1)"),
+    "ledger_stage2_grad_unsharded": ("    if stage >= 2:\n        g /= n", "    if stage >= 3:\n        g /= n"),
+    "padding_rule": ("psi_pad = ((psi + q - 1) // q) * q", "psi_pad = ((psi + q) // q) * q"),
+    "gather_order": ("full = np.concatenate(list(shards))", "full = np.concatenate(list(shards)[::-1])"),
+    "offload_not_accumulated": ("acc = r if acc is None else _chk32(acc + r)", "acc = r"),
+    "accumulate_mode_drops_acc": ("return _chk32(acc + reduce_full(rank_grads, weights))",
+                                  "return _chk32(reduce_full(rank_grads, weights))"),
+}
+
+
+@pytest.fixture(scope="module")
+def oracle_src():
+    with open(os.path.join(ROOT, "oracle", "zero_oracle.py")) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, oracle_src, tmp_path):
+    old, new = MUTATIONS[name]
+    assert old in oracle_src, f"mutation anchor for {name} no longer in the oracle"
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle",
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    (tmp_path / "oracle" / "zero_oracle.py").write_text(oracle_src.replace(old, new, 1))
+    for d in ("tests", "synthetic"):
+        os.symlink(os.path.join(ROOT, d), tmp_path / d)
+    r = subprocess.run(
+        [sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", "tests",
+         "-m", "not gpu", "-k", "oracle and not brute and not mutations"],
+        cwd=tmp_path, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 1, f"planted mistake {name} was not caught:\n{r.stdout[-2000:]}"
