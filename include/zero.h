@@ -1,0 +1,213 @@
+/*
+ * zero.h -- C ABI of libzero: the ZeRO sharded update on one MI355X (gfx950).
+ *
+ * N data-parallel ranks are simulated as N buffers in one GPU's HBM.  The
+ * library reduces the ranks' BF16 gradient contributions element-wise in FP32
+ * and hands each owner its 1/N slice (reduce-scatter), applies the owner's
+ * fused mixed-precision Adam/AdamW update to its FP32 master, m and v shards
+ * and writes its BF16 working-weight shard, gathers BF16 shards into a
+ * temporary full per-layer view (all-gather), and streams a gradient shard
+ * that lives in pinned host memory through two device slots (offload).
+ *
+ * The method is described on three web pages, cited below by title and
+ * section:
+ *   [slide] "分担数据，与分担保存责任，是两个动作" (beats b0-b3, notes 原 N46-N48)
+ *   [essay] "把训练账本放进多张设备" (sections 从持久状态开始记账,
+ *           数据分工与保存分工, ZeRO-3 的一次完整计算)
+ *   [blog]  "数据并行与 ZeRO：三级分片各省多少" (sections 每个参数 16 字节,
+ *           三级分片, 分片放到 CPU：两个缓冲就够)
+ *
+ * Conventions shared by every call:
+ *  - Device buffers are plain device pointers; the library never allocates,
+ *    frees or takes ownership of any caller buffer.  Host arrays (pointer
+ *    tables, weights, counts, hyper-parameters) are read during the call only.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *    compute call is asynchronous on that stream and does not synchronise.
+ *  - Each call validates all its arguments before launching anything; on a
+ *    validation failure nothing is launched and nothing is written.
+ *  - Return value: ZERO_OK (0) or a negative zero_status.  zero_last_error()
+ *    gives a message for the last failure on the calling thread.
+ *  - Element counts of 0 are valid and launch nothing; the buffer pointers of
+ *    such a call are not used and may be NULL (the pointer tables may not).
+ *  - Input and output buffers must not overlap, except where a call says so.
+ *  - Floating point: binary32 arithmetic with one rounding per operation (no
+ *    contraction into FMA), correctly rounded division and square root, FP32
+ *    subnormals preserved; BF16 values are rounded to nearest-even.  Results
+ *    are therefore the same bits on every call with the same inputs.
+ *  - Calls on different streams are independent; an offload handle must not be
+ *    used from two threads at once.
+ */
+#ifndef ZERO_H
+#define ZERO_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZERO_MAX_RANKS 16   /* upper bound on n_ranks and n_shards */
+
+typedef enum zero_status {
+  ZERO_OK = 0,
+  ZERO_ERR_ARG = -1,    /* null pointer, count out of range, overlapping buffers, bad hyper-parameter */
+  ZERO_ERR_ALIGN = -2,  /* a pointer is not aligned to its element size */
+  ZERO_ERR_SIZE = -3,   /* sizes inconsistent with each other */
+  ZERO_ERR_HIP = -4,    /* the HIP runtime reported an error (see zero_last_error) */
+  ZERO_ERR_STATE = -5   /* an offload handle was used out of order */
+} zero_status;
+
+/* Adam / AdamW hyper-parameters of one update.  step is t >= 1. */
+typedef struct zero_adam_hparams {
+  float lr, beta1, beta2, eps, weight_decay;
+  int64_t step;
+} zero_adam_hparams;
+
+/* The per-step scalars the update kernel uses, all binary32:
+ * one_minus_beta_i = 1 - beta_i (a float32 subtraction),
+ * bias_correction_i = float32(1 - double(beta_i)^step). */
+typedef struct zero_adam_scalars {
+  float lr, beta1, beta2, one_minus_beta1, one_minus_beta2;
+  float bias_correction1, bias_correction2, eps, weight_decay;
+} zero_adam_scalars;
+
+/* ---------------------------------------------------------------- host-side metadata */
+
+/* Fill `out` with the scalars that zero_adam_shard_step uses for `hp`.
+ * Errors: ZERO_ERR_ARG if a pointer is NULL, hp->step < 1, or a beta is not
+ * in [0, 1). */
+int zero_adam_scalars_compute(const zero_adam_hparams* hp, zero_adam_scalars* out);
+
+/* Loss-normalisation weights of the reduction ([slide] note 原 N48: scale the
+ * reduction to match the objective; [essay] 数据分工与保存分工: ranks with
+ * different sample or token counts must not be weighted blindly alike).
+ * counts == NULL: w_r = 1/n_ranks (batch mean).  Otherwise
+ * w_r = float32(double(counts[r]) / double(sum counts)).
+ * weights_out: host array of n_ranks floats.
+ * Errors: ZERO_ERR_ARG for NULL weights_out, n_ranks outside [1, 16], a
+ * negative count or a zero sum. */
+int zero_rank_weights(const int64_t* counts, int n_ranks, float* weights_out);
+
+/* Flatten/pad/partition layout of one unit ([slide] note 原 N46: owner shards
+ * are slices of the parameters, not layers; [blog] 三级分片: each owner holds
+ * 1/N).  psi = sum of numels; psi_pad = psi rounded up to a multiple of
+ * n_shards*256; shard_numel = psi_pad / n_shards.  Shard k of the flat vector
+ * is [k*shard_numel, (k+1)*shard_numel).
+ * Errors: ZERO_ERR_ARG for NULL outputs, numels == NULL with n_tensors > 0,
+ * n_shards outside [1, 16] or a negative numel; ZERO_ERR_SIZE on overflow. */
+int zero_shard_layout(const int64_t* numels, int n_tensors, int n_shards,
+                      int64_t* psi, int64_t* psi_pad, int64_t* shard_numel);
+
+/* ---------------------------------------------------------------- device calls */
+
+/* Reduce-scatter ([slide] note 原 N48; [essay] ZeRO-3 的一次完整计算;
+ * [blog] 三级分片, ZeRO-2): the contributions of every rank to the SAME
+ * parameter are combined element-wise, and owner k receives only its slice.
+ *
+ *   rank_grads   host array of n_ranks device pointers; rank r's contribution
+ *                is `numel` BF16 values (bit patterns) at rank_grads[r].
+ *   rank_weights host array of n_ranks floats (see zero_rank_weights).
+ *   shards_out   host array of n_shards device pointers to FP32 buffers of
+ *                numel/n_shards elements each.
+ *   accumulate   0: out = red;  1: out = out + red   (in place).
+ *
+ * For element i of shard k (global index j = k*numel/n_shards + i):
+ *   red = w_0*x_0[j];  red = red + w_r*x_r[j] for r = 1..n_ranks-1,
+ * with x_r the exact FP32 widening of the BF16 value: a fixed rank order, so
+ * the result is bitwise reproducible.  n_shards = 1 with pre-sliced
+ * contributions is the owner-local form (buckets, offload chunks).
+ * Errors: ZERO_ERR_ARG (NULL pointers, n_ranks or n_shards outside [1, 16],
+ * numel < 0, buffers overlapping), ZERO_ERR_SIZE (numel % n_shards != 0),
+ * ZERO_ERR_ALIGN (a BF16 pointer not 2-byte or FP32 pointer not 4-byte
+ * aligned), ZERO_ERR_HIP (launch failure). */
+int zero_reduce_scatter(const uint16_t* const* rank_grads, const float* rank_weights, int n_ranks,
+                        int64_t numel, float* const* shards_out, int n_shards, int accumulate,
+                        void* stream);
+
+/* Owner update: one fused pass of mixed-precision Adam/AdamW over n elements
+ * of the owner's shard ([slide] note 原 N48: the owner updates its master
+ * weights and m/v with the combined gradient; [essay] 从持久状态开始记账 and
+ * [blog] 每个参数 16 字节: FP32 master, two FP32 moments, BF16 working weight).
+ *
+ *   master, exp_avg, exp_avg_sq  FP32[n] device, updated in place.
+ *   bf16_out                     BF16[n] device, written: the new working weights.
+ *   grad                         FP32[n] device, read (the reduced gradient shard).
+ *
+ * Per element, with the scalars of zero_adam_scalars_compute:
+ *   m' = b1*m + (1-b1)*g;  v' = b2*v + (1-b2)*(g*g);
+ *   u = (m'/bc1) / (sqrt(v'/bc2) + eps);  if wd != 0: u = u + wd*p;
+ *   p' = p - lr*u;  bf16_out = round_to_nearest_even_bf16(p').
+ * Non-finite values propagate by IEEE rules (no clipping or skipping).
+ * Errors: ZERO_ERR_ARG (NULL, n < 0, overlap, bad hyper-parameters),
+ * ZERO_ERR_ALIGN, ZERO_ERR_HIP. */
+int zero_adam_shard_step(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* bf16_out,
+                         const float* grad, int64_t n, const zero_adam_hparams* hp, void* stream);
+
+/* All-gather into a temporary full view ([slide] note 原 N47 and beat b2;
+ * [essay] ZeRO-3 的一次完整计算; [blog] 三级分片, ZeRO-3): the owners'
+ * shards, concatenated in owner order, form the full per-layer view.
+ *
+ *   shards       host array of n_shards device pointers, shard_bytes each.
+ *   full_view    device buffer of n_shards*shard_bytes bytes, written; owned
+ *                by the caller, who releases it after use.
+ * A byte copy, so it serves any element type.  Errors: ZERO_ERR_ARG (NULL,
+ * n_shards outside [1, 16], shard_bytes < 0, overlap), ZERO_ERR_HIP. */
+int zero_all_gather_layer(const void* const* shards, int n_shards, int64_t shard_bytes,
+                          void* full_view, void* stream);
+
+/* ---------------------------------------------------------------- host-offloaded gradient shard */
+
+/* Two device slots stream a gradient shard that lives in pinned host memory
+ * ([blog] 分片放到 CPU：两个缓冲就够): chunk c of the shard uses slot c % 2.
+ *
+ * Caller-owned buffers, all given at creation:
+ *   host_shard_pinned  FP32[shard_numel] pinned host memory (the accumulator).
+ *   slot_contrib[s]    device BF16 buffer of n_ranks*chunk_numel values: rank
+ *                      r's contribution to the chunk in slot s starts at
+ *                      slot_contrib[s] + r*chunk_numel (a partial last chunk
+ *                      uses the first elements of each rank's range).
+ *   slot_f32[s]        device FP32 buffer of chunk_numel values (staging).
+ * The handle owns two side streams (host-to-device, device-to-host) and
+ * events only.
+ *
+ * zero_offload_stream(op = ZERO_OFFLOAD_REDUCE, chunk c, micro_batch mb):
+ *   the caller has written chunk c's contributions into slot_contrib[c % 2] on
+ *   compute_stream.  mb == 0: staging = red(c).  mb > 0: the host chunk is
+ *   copied in, staging = staging + red(c).  Then staging is copied to the
+ *   host chunk asynchronously.  red is zero_reduce_scatter's reduction with
+ *   rank_weights.  When the call returns the caller may write the next
+ *   contributions for slot c % 2 on compute_stream.
+ * zero_offload_stream(op = ZERO_OFFLOAD_ADAM, chunk c):
+ *   the host chunk is copied into slot_f32[c % 2] and zero_adam_shard_step runs
+ *   on it with the chunk's elements of master/exp_avg/exp_avg_sq/bf16_out
+ *   (device pointers to the whole shard).
+ * zero_offload_sync: waits for every queued copy and kernel of the handle; the
+ *   host shard may be read after it returns.
+ * Errors: ZERO_ERR_ARG / ZERO_ERR_ALIGN / ZERO_ERR_SIZE for bad arguments,
+ * ZERO_ERR_STATE for a chunk out of range, a REDUCE with mb > 0 for a chunk
+ * that has no earlier micro-batch, or an ADAM for a chunk never reduced;
+ * ZERO_ERR_HIP on runtime failures. */
+typedef struct zero_offload zero_offload;
+enum { ZERO_OFFLOAD_REDUCE = 0, ZERO_OFFLOAD_ADAM = 1 };
+
+int zero_offload_create(int n_ranks, int64_t shard_numel, int64_t chunk_numel,
+                        float* host_shard_pinned, uint16_t* const slot_contrib[2],
+                        float* const slot_f32[2], zero_offload** out);
+int zero_offload_stream(zero_offload* h, int op, int64_t chunk, int micro_batch,
+                        const float* rank_weights, float* master, float* exp_avg,
+                        float* exp_avg_sq, uint16_t* bf16_out, const zero_adam_hparams* hp,
+                        void* compute_stream);
+int zero_offload_sync(zero_offload* h);
+int zero_offload_destroy(zero_offload* h);
+
+/* ---------------------------------------------------------------- diagnostics */
+const char* zero_status_string(int status);
+const char* zero_last_error(void);
+/* 1 if the last device call took the 16-byte vector path, 0 for the scalar
+ * path (used by tests to cover both paths). */
+int zero_last_path_vectorized(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZERO_H */

@@ -1,0 +1,48 @@
+"""Helpers shared by the GPU parity tests: host<->device copies of BF16 bit
+patterns and FP32 arrays, and the parity bar."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle.compare import bits_equal_f32, max_ulp_bf16, max_ulp_f32
+
+# The bar: reduced gradients bit-exact; FP32 master/m/v within 2 ulp; BF16
+# working weights within 1 bf16 ulp.
+FP32_ULP_TOL = 2
+BF16_ULP_TOL = 1
+
+DEV = "cuda"
+
+
+def bf16_to_dev(bits: np.ndarray, device=DEV) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def f32_to_dev(x: np.ndarray, device=DEV) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+def bf16_to_host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def f32_to_host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().cpu().numpy()
+
+
+def assert_grad_exact(gpu: np.ndarray, ref: np.ndarray, what="reduced gradient"):
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    if not bits_equal_f32(gpu, ref):
+        bad = np.nonzero(gpu.view(np.uint32) != ref.view(np.uint32))[0]
+        i = bad[0]
+        raise AssertionError(f"{what} not bit-exact at {bad.size} elements; first {i}: "
+                             f"gpu {gpu[i]!r} oracle {ref[i]!r}")
+
+
+def assert_state_close(p, m, v, b, ref, what=""):
+    """ref = (p', m', v', bf16 bits) from the oracle.  Returns the max ulps."""
+    u = (max_ulp_f32(p, ref[0]), max_ulp_f32(m, ref[1]), max_ulp_f32(v, ref[2]))
+    ub = max_ulp_bf16(b, ref[3])
+    assert max(u) <= FP32_ULP_TOL and ub <= BF16_ULP_TOL, f"{what}: ulps master/m/v {u}, bf16 {ub}"
+    return u, ub

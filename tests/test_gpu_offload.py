@@ -1,0 +1,94 @@
+"""GPU parity of the two-slot host-offload engine (zero_offload_*): the pinned
+host shard after M micro-batches equals the oracle's accumulation, the state
+after the streamed-back update equals the oracle's Adam on it, and the result
+does not change when the side streams are delayed or released staging buffers
+are poisoned (so a missing wait would show up as a wrong or NaN value)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as S
+from gpu_helpers import assert_grad_exact, assert_state_close, bf16_to_dev, bf16_to_host, f32_to_host
+
+pytestmark = pytest.mark.gpu
+
+z = pytest.importorskip("zero_sharded_optimizer_reduce_amd")
+from zero_sharded_optimizer_reduce_amd.drivers import OffloadStep  # noqa: E402
+
+
+def _run(shard, chunk, n_ranks=4, n_micro=4, seed=0, env=None):
+    env = env or {}
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update(env)
+    try:
+        st = OffloadStep(shard, n_ranks, chunk, device="cuda")
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    g = S.rng(seed)
+    contrib = [[[S.bf16_normal(g, st.chunk_len(c), 1e-3) for _ in range(n_ranks)]
+                for c in range(st.n_chunks)] for _ in range(n_micro)]
+    pool = [[[bf16_to_dev(x) for x in rc] for rc in mb] for mb in contrib]
+    p0, m0, v0 = S.host_state(seed + 1, shard, 0.02)
+    st.master.copy_(torch.from_numpy(p0))
+    w = np.full(n_ranks, 1.0 / (n_ranks * n_micro), np.float32)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, step=1)
+
+    def produce(mb, c, views):
+        for r, vw in enumerate(views):
+            vw.copy_(pool[mb][c][r])
+
+    st.step(produce, n_micro, w, hp)
+    st.sync()
+    torch.cuda.synchronize()
+    host = st.host.numpy().copy()
+    sc = oracle.adam_scalars(1e-3, 0.9, 0.999, 1e-8, 0.0, 1)
+    for c in range(st.n_chunks):
+        lo, hi = c * chunk, c * chunk + st.chunk_len(c)
+        acc = oracle.offload_accumulate([contrib[mb][c] for mb in range(n_micro)], w)
+        assert_grad_exact(host[lo:hi], acc, f"host chunk {c}")
+        ref = oracle.adam_step(p0[lo:hi], m0[lo:hi], v0[lo:hi], acc, sc)
+        assert_state_close(f32_to_host(st.master[lo:hi]), f32_to_host(st.exp_avg[lo:hi]),
+                           f32_to_host(st.exp_avg_sq[lo:hi]), bf16_to_host(st.bf16[lo:hi]), ref,
+                           f"chunk {c}")
+    st.engine.close()
+
+
+@pytest.mark.parametrize("shard,chunk", [(3 * 8192 + 1000, 8192), (8192, 8192), (5 * 1000 + 7, 1000),
+                                         (1, 1 << 10), (9 * 4096, 4096)])
+def test_offload_matches_oracle(shard, chunk):
+    print(f"offload shard={shard} chunk={chunk}", flush=True)
+    _run(shard, chunk)
+
+
+def test_offload_with_delayed_side_streams_and_poison():
+    _run(7 * 4096 + 123, 4096, env={"ZERO_OFFLOAD_DEBUG_DELAY_US": "3000",
+                                    "ZERO_OFFLOAD_DEBUG_POISON": "1"}, seed=5)
+
+
+def test_offload_single_micro_batch_and_ranks():
+    _run(4 * 2048, 2048, n_ranks=1, n_micro=1, seed=7)
+    _run(4 * 2048 + 8, 2048, n_ranks=3, n_micro=2, seed=8)
+
+
+def test_offload_misuse_is_rejected():
+    st = OffloadStep(4 * 1024, 4, 1024, device="cuda")
+    w = np.full(4, 0.25, np.float32)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, step=1)
+    for v in st.slot_contrib:
+        v.zero_()
+    with pytest.raises(z.ZeroError, match="ZERO_ERR_STATE"):
+        st.engine.reduce(0, 1, w)                 # micro-batch 1 before micro-batch 0
+    with pytest.raises(z.ZeroError, match="ZERO_ERR_STATE"):
+        st.engine.adam(1, st.master, st.exp_avg, st.exp_avg_sq, st.bf16, hp)   # never reduced
+    with pytest.raises(z.ZeroError, match="ZERO_ERR_STATE"):
+        st.engine.reduce(4, 0, w)                 # chunk out of range
+    st.engine.reduce(0, 0, w)
+    st.sync()
+    st.engine.close()

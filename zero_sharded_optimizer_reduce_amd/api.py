@@ -1,0 +1,219 @@
+"""Thin Python binding of libzero's C ABI (include/zero.h), same names.
+
+Argument marshalling only: tensors are checked for device, dtype, layout and
+size (the C ABI sees raw pointers and cannot), their data pointers and the
+current HIP stream are passed through, and every computation runs in the HIP
+kernels.  PyTorch provides device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Mapping, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import AdamHparams, check, load
+
+_BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, what: str, dtypes) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: must be a device tensor, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{what}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    return t.data_ptr()
+
+
+def _ptrs(ptrs) -> C.Array:
+    return (C.c_void_p * len(ptrs))(*ptrs)
+
+
+def hparams(hp) -> AdamHparams:
+    if isinstance(hp, AdamHparams):
+        return hp
+    return AdamHparams(float(hp["lr"]), float(hp["beta1"]), float(hp["beta2"]), float(hp["eps"]),
+                       float(hp.get("weight_decay", 0.0)), int(hp["step"]))
+
+
+# ------------------------------------------------------------ host metadata
+def zero_adam_scalars_compute(hp) -> dict:
+    out = _lib.AdamScalars()
+    check(load().zero_adam_scalars_compute(C.byref(hparams(hp)), C.byref(out)), "zero_adam_scalars_compute")
+    return {name: np.float32(getattr(out, name)) for name, _ in _lib.AdamScalars._fields_}
+
+
+def zero_rank_weights(counts: Optional[Sequence[int]], n_ranks: int) -> np.ndarray:
+    out = (C.c_float * n_ranks)()
+    arr = None if counts is None else (C.c_int64 * n_ranks)(*[int(c) for c in counts])
+    if counts is not None and len(counts) != n_ranks:
+        raise ValueError("zero_rank_weights: len(counts) != n_ranks")
+    check(load().zero_rank_weights(arr, n_ranks, out), "zero_rank_weights")
+    return np.array(list(out), dtype=np.float32)
+
+
+def zero_shard_layout(numels: Sequence[int], n_shards: int):
+    arr = (C.c_int64 * max(1, len(numels)))(*[int(n) for n in numels])
+    psi, pad, s = C.c_int64(), C.c_int64(), C.c_int64()
+    check(load().zero_shard_layout(arr, len(numels), n_shards, C.byref(psi), C.byref(pad), C.byref(s)),
+          "zero_shard_layout")
+    return psi.value, pad.value, s.value
+
+
+# ------------------------------------------------------------ device calls
+def zero_reduce_scatter(rank_grads: Sequence[torch.Tensor], rank_weights, shards_out: Sequence[torch.Tensor],
+                        accumulate: bool = False, stream=None) -> None:
+    """Owner k's shard = sum_r w_r * float(rank_grads[r][k*S:(k+1)*S]) (rank order),
+    or shard += that sum when accumulate.  rank_grads: BF16 device tensors of
+    equal numel; shards_out: FP32 device tensors of numel/len(shards_out) each."""
+    n_ranks, n_shards = len(rank_grads), len(shards_out)
+    if n_ranks < 1 or n_shards < 1:
+        raise ValueError("zero_reduce_scatter: need at least one rank and one shard")
+    numel = rank_grads[0].numel()
+    gp = [_dev(g, f"rank_grads[{r}]", _BF16_LIKE) for r, g in enumerate(rank_grads)]
+    if any(g.numel() != numel for g in rank_grads):
+        raise ValueError("zero_reduce_scatter: rank contributions differ in size")
+    if numel % n_shards:
+        raise ValueError("zero_reduce_scatter: numel not divisible by the number of shards")
+    op = [_dev(s, f"shards_out[{k}]", (torch.float32,)) for k, s in enumerate(shards_out)]
+    if any(s.numel() != numel // n_shards for s in shards_out):
+        raise ValueError("zero_reduce_scatter: each shard must hold numel/n_shards elements")
+    w = np.ascontiguousarray(np.asarray(rank_weights, dtype=np.float32))
+    if w.size != n_ranks:
+        raise ValueError("zero_reduce_scatter: one weight per rank")
+    check(load().zero_reduce_scatter(_ptrs(gp), w.ctypes.data_as(_lib.FP), n_ranks, numel, _ptrs(op),
+                                     n_shards, int(bool(accumulate)), _stream(stream)),
+          "zero_reduce_scatter")
+
+
+def zero_adam_shard_step(master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor,
+                         bf16_out: torch.Tensor, grad: torch.Tensor, hp, stream=None) -> None:
+    """Fused Adam/AdamW owner update in place (master, m, v FP32; bf16_out written)."""
+    n = master.numel()
+    ptrs = [_dev(master, "master", (torch.float32,)), _dev(exp_avg, "exp_avg", (torch.float32,)),
+            _dev(exp_avg_sq, "exp_avg_sq", (torch.float32,)), _dev(bf16_out, "bf16_out", _BF16_LIKE),
+            _dev(grad, "grad", (torch.float32,))]
+    if any(t.numel() != n for t in (exp_avg, exp_avg_sq, bf16_out, grad)):
+        raise ValueError("zero_adam_shard_step: all buffers must have the same numel")
+    h = hparams(hp)
+    check(load().zero_adam_shard_step(*ptrs, n, C.byref(h), _stream(stream)), "zero_adam_shard_step")
+
+
+def zero_all_gather_layer(shards: Sequence[torch.Tensor], full_view: torch.Tensor, stream=None) -> None:
+    """full_view = concatenation of the shards' bytes in owner order."""
+    n = len(shards)
+    if n < 1:
+        raise ValueError("zero_all_gather_layer: no shards")
+    nbytes = shards[0].numel() * shards[0].element_size()
+    sp = [_dev(s, f"shards[{k}]", (s.dtype,)) for k, s in enumerate(shards)]
+    if any(s.numel() * s.element_size() != nbytes for s in shards):
+        raise ValueError("zero_all_gather_layer: shards differ in size")
+    vp = _dev(full_view, "full_view", (full_view.dtype,))
+    if full_view.numel() * full_view.element_size() != n * nbytes:
+        raise ValueError("zero_all_gather_layer: full_view must hold exactly n_shards*shard_bytes bytes")
+    check(load().zero_all_gather_layer(_ptrs(sp), n, nbytes, vp, _stream(stream)), "zero_all_gather_layer")
+
+
+def zero_last_path_vectorized() -> int:
+    return int(load().zero_last_path_vectorized())
+
+
+# ------------------------------------------------------------ offload engine
+class ZeroOffload:
+    """Two-slot host-offloaded gradient shard (zero_offload_* in include/zero.h).
+
+    host_shard: pinned FP32 CPU tensor [shard_numel]; slot_contrib: two BF16
+    device tensors [n_ranks*chunk_numel]; slot_f32: two FP32 device tensors
+    [chunk_numel].  The tensors must outlive the handle."""
+
+    def __init__(self, n_ranks: int, shard_numel: int, chunk_numel: int, host_shard: torch.Tensor,
+                 slot_contrib: Sequence[torch.Tensor], slot_f32: Sequence[torch.Tensor]):
+        if host_shard.device.type != "cpu" or host_shard.dtype != torch.float32 or not host_shard.is_contiguous():
+            raise ValueError("host_shard: contiguous float32 CPU tensor required")
+        if not host_shard.is_pinned():
+            raise ValueError("host_shard: must be pinned host memory")
+        if host_shard.numel() != shard_numel:
+            raise ValueError("host_shard: numel != shard_numel")
+        if len(slot_contrib) != 2 or len(slot_f32) != 2:
+            raise ValueError("two slots required")
+        cp = [_dev(t, f"slot_contrib[{s}]", _BF16_LIKE) for s, t in enumerate(slot_contrib)]
+        fp = [_dev(t, f"slot_f32[{s}]", (torch.float32,)) for s, t in enumerate(slot_f32)]
+        if any(t.numel() != n_ranks * chunk_numel for t in slot_contrib):
+            raise ValueError("slot_contrib: numel must be n_ranks*chunk_numel")
+        if any(t.numel() != chunk_numel for t in slot_f32):
+            raise ValueError("slot_f32: numel must be chunk_numel")
+        self._keep = (host_shard, tuple(slot_contrib), tuple(slot_f32))
+        self.n_ranks, self.shard_numel, self.chunk_numel = n_ranks, shard_numel, chunk_numel
+        self.n_chunks = -(-shard_numel // chunk_numel)
+        h = C.c_void_p()
+        check(load().zero_offload_create(n_ranks, shard_numel, chunk_numel, host_shard.data_ptr(),
+                                         _ptrs(cp), _ptrs(fp), C.byref(h)), "zero_offload_create")
+        self._h = h
+
+    def chunk_len(self, c: int) -> int:
+        return min(self.chunk_numel, self.shard_numel - c * self.chunk_numel)
+
+    def reduce(self, chunk: int, micro_batch: int, rank_weights, stream=None) -> None:
+        w = np.ascontiguousarray(np.asarray(rank_weights, dtype=np.float32))
+        if w.size != self.n_ranks:
+            raise ValueError("one weight per rank")
+        check(load().zero_offload_stream(self._h, _lib.ZERO_OFFLOAD_REDUCE, chunk, micro_batch,
+                                         w.ctypes.data_as(_lib.FP), None, None, None, None, None,
+                                         _stream(stream)), "zero_offload_stream(REDUCE)")
+
+    def adam(self, chunk: int, master, exp_avg, exp_avg_sq, bf16_out, hp, stream=None) -> None:
+        ptrs = [_dev(master, "master", (torch.float32,)), _dev(exp_avg, "exp_avg", (torch.float32,)),
+                _dev(exp_avg_sq, "exp_avg_sq", (torch.float32,)), _dev(bf16_out, "bf16_out", _BF16_LIKE)]
+        if any(t.numel() != self.shard_numel for t in (master, exp_avg, exp_avg_sq, bf16_out)):
+            raise ValueError("state tensors must cover the whole shard")
+        h = hparams(hp)
+        check(load().zero_offload_stream(self._h, _lib.ZERO_OFFLOAD_ADAM, chunk, 0, None, *ptrs,
+                                         C.byref(h), _stream(stream)), "zero_offload_stream(ADAM)")
+
+    def sync(self) -> None:
+        check(load().zero_offload_sync(self._h), "zero_offload_sync")
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            st = load().zero_offload_destroy(self._h)
+            self._h = None
+            check(st, "zero_offload_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def zero_offload_create(n_ranks, shard_numel, chunk_numel, host_shard, slot_contrib, slot_f32) -> ZeroOffload:
+    return ZeroOffload(n_ranks, shard_numel, chunk_numel, host_shard, slot_contrib, slot_f32)
+
+
+def zero_offload_stream(h: ZeroOffload, op: int, chunk: int, micro_batch: int = 0, rank_weights=None,
+                        master=None, exp_avg=None, exp_avg_sq=None, bf16_out=None, hp=None, stream=None):
+    if op == _lib.ZERO_OFFLOAD_REDUCE:
+        return h.reduce(chunk, micro_batch, rank_weights, stream)
+    return h.adam(chunk, master, exp_avg, exp_avg_sq, bf16_out, hp, stream)
+
+
+def zero_offload_sync(h: ZeroOffload) -> None:
+    h.sync()
+
+
+def zero_offload_destroy(h: ZeroOffload) -> None:
+    h.close()

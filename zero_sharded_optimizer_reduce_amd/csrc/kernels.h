@@ -1,0 +1,52 @@
+// Internal launch interface between the C ABI (zero_api.cpp, offload.cpp) and
+// the gfx950 kernels (kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/zero.h"
+
+namespace zero {
+
+struct RsParams {
+  const uint16_t* g[ZERO_MAX_RANKS];  // rank contributions, numel BF16 each
+  float w[ZERO_MAX_RANKS];            // rank weights
+  float* out[ZERO_MAX_RANKS];         // owner shards, `shard` FP32 each
+  int64_t shard;                      // elements per owner shard
+  int n_ranks;
+};
+
+struct AdamParams {
+  float* p;
+  float* m;
+  float* v;
+  uint16_t* b;
+  const float* g;
+  int64_t n;
+  zero_adam_scalars s;
+};
+
+struct GatherParams {
+  const void* src[ZERO_MAX_RANKS];
+  void* dst;
+  int64_t shard_bytes;
+};
+
+// Each launcher enqueues on `stream` and returns hipSuccess or the launch
+// error.  `vec` selects the 128-bit path; the caller has checked that every
+// pointer and per-shard offset it uses is 16-byte aligned.
+hipError_t launch_reduce_scatter(const RsParams& p, int n_shards, bool accumulate, bool vec,
+                                 hipStream_t stream);
+hipError_t launch_adam(const AdamParams& p, bool vec, hipStream_t stream);
+hipError_t launch_gather(const GatherParams& p, int n_shards, int path, hipStream_t stream);
+
+// Fill n 32-bit words with `value` (used to poison released staging buffers
+// in the offload engine's debug mode).
+hipError_t launch_fill_u32(uint32_t* p, uint32_t value, int64_t n, hipStream_t stream);
+
+// Gather path selector: 16-byte, 4-byte or 1-byte units.
+enum { GATHER_V16 = 0, GATHER_U32 = 1, GATHER_U8 = 2 };
+
+}  // namespace zero

@@ -1,0 +1,353 @@
+// gfx950 kernels of the sharded update: reduce-scatter, fused Adam owner
+// update, all-gather copy.  All three are HBM-streaming kernels (no data
+// reuse, a few FLOPs per byte), so they use no LDS and no MFMA: each lane
+// moves 16-byte vectors with non-temporal loads and stores, 256-lane
+// workgroups (four wave64s) walk the arrays in a grid-stride loop, and the
+// grid is sized from the device's CU count so that every CU stays busy.
+//
+// Floating point: the file is compiled with FP contraction off (also forced
+// below), so every multiply and add is its own binary32 rounding; '/' and
+// sqrtf are the correctly rounded forms (hipcc's default).  The arithmetic is
+// therefore the same, operation for operation, as the definitions cited at
+// each kernel.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+
+#include "kernels.h"
+
+#pragma clang fp contract(off)
+
+namespace zero {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = 256;
+
+// ------------------------------------------------------------------ helpers
+// A BF16 value is the high half of a binary32, so widening is a shift (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_at(const uint16_t* p, int64_t i) {
+  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+
+// Round-to-nearest-even binary32 -> bfloat16 (gfx950 converts in hardware).
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+__device__ __forceinline__ uint32_t to_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(to_bf16(lo)) | (static_cast<uint32_t>(to_bf16(hi)) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_load(p); }
+template <typename T>
+__device__ __forceinline__ void st_nt(T v, T* p) { __builtin_nontemporal_store(v, p); }
+
+// ------------------------------------------------------------ reduce-scatter
+// Owner k, element i (global index j = k*shard + i):
+//   red = w_0*x_0[j]; red = red + w_r*x_r[j] for r = 1..N-1 (rank order),
+// optionally out = out + red.  Contributions of one parameter are combined
+// element-wise and never mixed with other parameters; the owner receives only
+// its slice (slide "分担数据，与分担保存责任，是两个动作", note 原 N48).
+//
+// Vector path: one 16-byte load per rank gives 8 BF16 values; the 8 FP32
+// results leave as two 16-byte stores.  U vectors per lane per iteration keep
+// N*U loads in flight before the first use.
+template <int N, bool ACC, int U>
+__global__ __launch_bounds__(kBlock) void rs_vec_kernel(RsParams p) {
+  constexpr int NMAX = N > 0 ? N : ZERO_MAX_RANKS;
+  const int n = N > 0 ? N : p.n_ranks;
+  const int k = blockIdx.y;
+  const int64_t nvec = p.shard >> 3;
+  const int64_t off = static_cast<int64_t>(k) * nvec;
+  f32x4* __restrict__ out = reinterpret_cast<f32x4*>(p.out[k]);
+  const int64_t step = static_cast<int64_t>(gridDim.x) * kBlock * U;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock * U + threadIdx.x; base < nvec;
+       base += step) {
+    u32x4 x[U][NMAX];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * kBlock;
+#pragma unroll
+      for (int r = 0; r < NMAX; ++r)
+        if (r < n && i < nvec) x[u][r] = ld_nt(reinterpret_cast<const u32x4*>(p.g[r]) + off + i);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * kBlock;
+      if (i >= nvec) break;
+      float a[8];
+      const float w0 = p.w[0];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a[2 * q] = w0 * bf16_lo(x[u][0][q]);
+        a[2 * q + 1] = w0 * bf16_hi(x[u][0][q]);
+      }
+#pragma unroll
+      for (int r = 1; r < NMAX; ++r) {
+        if (r < n) {
+          const float wr = p.w[r];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            a[2 * q] = a[2 * q] + wr * bf16_lo(x[u][r][q]);
+            a[2 * q + 1] = a[2 * q + 1] + wr * bf16_hi(x[u][r][q]);
+          }
+        }
+      }
+      f32x4 lo = {a[0], a[1], a[2], a[3]};
+      f32x4 hi = {a[4], a[5], a[6], a[7]};
+      if (ACC) {
+        lo = out[2 * i] + lo;
+        hi = out[2 * i + 1] + hi;
+      }
+      st_nt(lo, out + 2 * i);
+      st_nt(hi, out + 2 * i + 1);
+    }
+  }
+}
+
+// Element-at-a-time path for shards whose length or pointers do not allow
+// 16-byte vectors.  Same arithmetic, same order.
+template <bool ACC>
+__global__ __launch_bounds__(kBlock) void rs_scalar_kernel(RsParams p) {
+  const int k = blockIdx.y;
+  const int64_t base = static_cast<int64_t>(k) * p.shard;
+  float* __restrict__ out = p.out[k];
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < p.shard;
+       i += static_cast<int64_t>(gridDim.x) * kBlock) {
+    float a = p.w[0] * bf16_at(p.g[0], base + i);
+    for (int r = 1; r < p.n_ranks; ++r) a = a + p.w[r] * bf16_at(p.g[r], base + i);
+    out[i] = ACC ? out[i] + a : a;
+  }
+}
+
+// ---------------------------------------------------------------- Adam update
+// The owner's update of its master weight p, first moment m and second moment
+// v with the reduced gradient g (slide, note 原 N48; essay "把训练账本放进多张
+// 设备", section 从持久状态开始记账): bias-corrected Adam with decoupled decay.
+template <bool WD>
+__device__ __forceinline__ void adam_elem(float& p, float& m, float& v, float g,
+                                          const zero_adam_scalars& s) {
+  const float m1 = s.beta1 * m + s.one_minus_beta1 * g;
+  const float gg = g * g;
+  const float v1 = s.beta2 * v + s.one_minus_beta2 * gg;
+  const float m_hat = m1 / s.bias_correction1;
+  const float v_hat = v1 / s.bias_correction2;
+  const float denom = sqrtf(v_hat) + s.eps;
+  float u = m_hat / denom;
+  if (WD) u = u + s.weight_decay * p;
+  p = p - s.lr * u;
+  m = m1;
+  v = v1;
+}
+
+// One pass: read g, p, m, v (16 B/param), write p, m, v and the BF16 working
+// weight (14 B/param).  Vector path: 4 elements per 16-byte access, U vectors
+// per lane per iteration; the n % 4 tail goes element-wise.
+template <bool WD, int U>
+__global__ __launch_bounds__(kBlock) void adam_vec_kernel(AdamParams a) {
+  const int64_t nvec = a.n >> 2;
+  f32x4* __restrict__ P = reinterpret_cast<f32x4*>(a.p);
+  f32x4* __restrict__ M = reinterpret_cast<f32x4*>(a.m);
+  f32x4* __restrict__ V = reinterpret_cast<f32x4*>(a.v);
+  const f32x4* __restrict__ G = reinterpret_cast<const f32x4*>(a.g);
+  u32x2* __restrict__ B = reinterpret_cast<u32x2*>(a.b);
+  const int64_t step = static_cast<int64_t>(gridDim.x) * kBlock * U;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock * U + threadIdx.x; base < nvec;
+       base += step) {
+    f32x4 g[U], p[U], m[U], v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * kBlock;
+      if (i < nvec) {
+        g[u] = ld_nt(G + i);
+        p[u] = ld_nt(P + i);
+        m[u] = ld_nt(M + i);
+        v[u] = ld_nt(V + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * kBlock;
+      if (i >= nvec) break;
+      float pe[4] = {p[u].x, p[u].y, p[u].z, p[u].w};
+      float me[4] = {m[u].x, m[u].y, m[u].z, m[u].w};
+      float ve[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      const float ge[4] = {g[u].x, g[u].y, g[u].z, g[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) adam_elem<WD>(pe[e], me[e], ve[e], ge[e], a.s);
+      st_nt(f32x4{pe[0], pe[1], pe[2], pe[3]}, P + i);
+      st_nt(f32x4{me[0], me[1], me[2], me[3]}, M + i);
+      st_nt(f32x4{ve[0], ve[1], ve[2], ve[3]}, V + i);
+      st_nt(u32x2{to_bf16x2(pe[0], pe[1]), to_bf16x2(pe[2], pe[3])}, B + i);
+    }
+  }
+  const int64_t tail = a.n - (nvec << 2);
+  if (blockIdx.x == 0 && threadIdx.x < tail) {
+    const int64_t i = (nvec << 2) + threadIdx.x;
+    float pe = a.p[i], me = a.m[i], ve = a.v[i];
+    adam_elem<WD>(pe, me, ve, a.g[i], a.s);
+    a.p[i] = pe;
+    a.m[i] = me;
+    a.v[i] = ve;
+    a.b[i] = to_bf16(pe);
+  }
+}
+
+template <bool WD>
+__global__ __launch_bounds__(kBlock) void adam_scalar_kernel(AdamParams a) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < a.n;
+       i += static_cast<int64_t>(gridDim.x) * kBlock) {
+    float pe = a.p[i], me = a.m[i], ve = a.v[i];
+    adam_elem<WD>(pe, me, ve, a.g[i], a.s);
+    a.p[i] = pe;
+    a.m[i] = me;
+    a.v[i] = ve;
+    a.b[i] = to_bf16(pe);
+  }
+}
+
+// ---------------------------------------------------------------- all-gather
+// The full view is the owners' shards concatenated in owner order (essay,
+// section ZeRO-3 的一次完整计算; slide, note 原 N47).  Owner k = blockIdx.y.
+template <typename T, int U>
+__global__ __launch_bounds__(kBlock) void gather_kernel(GatherParams p) {
+  const int k = blockIdx.y;
+  const int64_t n = p.shard_bytes / static_cast<int64_t>(sizeof(T));
+  const T* __restrict__ src = reinterpret_cast<const T*>(p.src[k]);
+  T* __restrict__ dst = reinterpret_cast<T*>(static_cast<char*>(p.dst) + k * p.shard_bytes);
+  const int64_t step = static_cast<int64_t>(gridDim.x) * kBlock * U;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock * U + threadIdx.x; base < n;
+       base += step) {
+    T x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (base + u * kBlock < n) x[u] = ld_nt(src + base + u * kBlock);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (base + u * kBlock < n) st_nt(x[u], dst + base + u * kBlock);
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void fill_u32_kernel(uint32_t* p, uint32_t value, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kBlock)
+    p[i] = value;
+}
+
+// -------------------------------------------------------------- launch shape
+int blocks_per_cu() {
+  static int v = [] {
+    const char* s = getenv("ZERO_BLOCKS_PER_CU");
+    int x = s ? atoi(s) : 0;
+    return (x >= 1 && x <= 64) ? x : 8;
+  }();
+  return v;
+}
+
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+// Blocks along x for `units` work items per owner, each block iteration
+// covering kBlock*u of them; the total over the n_y owners is capped at
+// blocks_per_cu() per CU (the rest is covered by the grid-stride loop).
+unsigned grid_x(int64_t units, int u, int n_y) {
+  const int64_t per_iter = static_cast<int64_t>(kBlock) * u;
+  int64_t need = (units + per_iter - 1) / per_iter;
+  int64_t cap = static_cast<int64_t>(device_cus()) * blocks_per_cu() / (n_y > 0 ? n_y : 1);
+  if (cap < 1) cap = 1;
+  if (need > cap) need = cap;
+  if (need < 1) need = 1;
+  return static_cast<unsigned>(need);
+}
+
+constexpr int kRsU = 2;
+constexpr int kAdamU = 2;
+constexpr int kGatherU = 4;
+
+template <int N, bool ACC>
+hipError_t rs_vec_launch(const RsParams& p, int n_shards, hipStream_t s) {
+  dim3 grid(grid_x(p.shard >> 3, kRsU, n_shards), n_shards);
+  hipLaunchKernelGGL((rs_vec_kernel<N, ACC, kRsU>), grid, dim3(kBlock), 0, s, p);
+  return hipGetLastError();
+}
+
+template <bool ACC>
+hipError_t rs_dispatch(const RsParams& p, int n_shards, bool vec, hipStream_t s) {
+  if (!vec) {
+    dim3 grid(grid_x(p.shard, 1, n_shards), n_shards);
+    hipLaunchKernelGGL((rs_scalar_kernel<ACC>), grid, dim3(kBlock), 0, s, p);
+    return hipGetLastError();
+  }
+  switch (p.n_ranks) {
+    case 1: return rs_vec_launch<1, ACC>(p, n_shards, s);
+    case 2: return rs_vec_launch<2, ACC>(p, n_shards, s);
+    case 4: return rs_vec_launch<4, ACC>(p, n_shards, s);
+    case 8: return rs_vec_launch<8, ACC>(p, n_shards, s);
+    default: return rs_vec_launch<0, ACC>(p, n_shards, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_reduce_scatter(const RsParams& p, int n_shards, bool accumulate, bool vec,
+                                 hipStream_t stream) {
+  return accumulate ? rs_dispatch<true>(p, n_shards, vec, stream)
+                    : rs_dispatch<false>(p, n_shards, vec, stream);
+}
+
+hipError_t launch_adam(const AdamParams& a, bool vec, hipStream_t s) {
+  const bool wd = a.s.weight_decay != 0.0f;
+  if (vec) {
+    dim3 grid(grid_x(a.n >> 2, kAdamU, 1));
+    if (wd)
+      hipLaunchKernelGGL((adam_vec_kernel<true, kAdamU>), grid, dim3(kBlock), 0, s, a);
+    else
+      hipLaunchKernelGGL((adam_vec_kernel<false, kAdamU>), grid, dim3(kBlock), 0, s, a);
+  } else {
+    dim3 grid(grid_x(a.n, 1, 1));
+    if (wd)
+      hipLaunchKernelGGL((adam_scalar_kernel<true>), grid, dim3(kBlock), 0, s, a);
+    else
+      hipLaunchKernelGGL((adam_scalar_kernel<false>), grid, dim3(kBlock), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherParams& p, int n_shards, int path, hipStream_t s) {
+  if (path == GATHER_V16) {
+    dim3 grid(grid_x(p.shard_bytes / 16, kGatherU, n_shards), n_shards);
+    hipLaunchKernelGGL((gather_kernel<u32x4, kGatherU>), grid, dim3(kBlock), 0, s, p);
+  } else if (path == GATHER_U32) {
+    dim3 grid(grid_x(p.shard_bytes / 4, kGatherU, n_shards), n_shards);
+    hipLaunchKernelGGL((gather_kernel<uint32_t, kGatherU>), grid, dim3(kBlock), 0, s, p);
+  } else {
+    dim3 grid(grid_x(p.shard_bytes, kGatherU, n_shards), n_shards);
+    hipLaunchKernelGGL((gather_kernel<uint8_t, kGatherU>), grid, dim3(kBlock), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t value, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_x(n, 1, 1)), dim3(kBlock), 0, s, p, value, n);
+  return hipGetLastError();
+}
+
+}  // namespace zero

@@ -1,0 +1,54 @@
+// Host-only argument checks of the C ABI (no HIP dependency, so they can be
+// built with g++ and run under the host sanitizers).  Every function returns
+// ZERO_OK or a negative zero_status and writes a message into `err`.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/zero.h"
+
+namespace zero {
+
+struct Err {
+  char msg[256];
+  Err() { msg[0] = 0; }
+};
+
+int set_err(Err& e, int status, const char* fmt, ...);
+
+// [lo, hi) byte ranges of device buffers, used for the overlap checks.
+struct Range {
+  uintptr_t lo, hi;
+};
+bool overlaps(Range a, Range b);
+
+int check_reduce_scatter(const uint16_t* const* rank_grads, const float* rank_weights,
+                         int n_ranks, int64_t numel, float* const* shards_out, int n_shards,
+                         int accumulate, Err& e);
+
+int check_adam_hparams(const zero_adam_hparams* hp, Err& e);
+
+int check_adam(const float* master, const float* exp_avg, const float* exp_avg_sq,
+               const uint16_t* bf16_out, const float* grad, int64_t n,
+               const zero_adam_hparams* hp, Err& e);
+
+int check_all_gather(const void* const* shards, int n_shards, int64_t shard_bytes,
+                     const void* full_view, Err& e);
+
+int check_offload_create(int n_ranks, int64_t shard_numel, int64_t chunk_numel,
+                         const float* host_shard, uint16_t* const slot_contrib[2],
+                         float* const slot_f32[2], Err& e);
+
+// Scalars the update kernel uses (binary32 values, see zero_adam_scalars).
+int adam_scalars(const zero_adam_hparams* hp, zero_adam_scalars* out, Err& e);
+
+int rank_weights(const int64_t* counts, int n_ranks, float* out, Err& e);
+
+int shard_layout(const int64_t* numels, int n_tensors, int n_shards, int64_t* psi,
+                 int64_t* psi_pad, int64_t* shard_numel, Err& e);
+
+// True when every pointer is 16-byte aligned: the kernels' 128-bit path.
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace zero

@@ -1,0 +1,140 @@
+// C ABI entry points of libzero (declared in include/zero.h): validate on the
+// host, pick the 16-byte or element-wise kernel path, launch on the caller's
+// stream.  No call allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+#include "validate.h"
+
+namespace zero {
+
+thread_local char g_last_error[320] = "";
+thread_local int g_last_vec = -1;
+
+int fail(int status, const char* msg) {
+  snprintf(g_last_error, sizeof g_last_error, "%s", msg);
+  return status;
+}
+
+int hip_status(hipError_t err, const char* where) {
+  if (err == hipSuccess) return ZERO_OK;
+  snprintf(g_last_error, sizeof g_last_error, "%s: %s", where, hipGetErrorString(err));
+  return ZERO_ERR_HIP;
+}
+
+void set_path(bool vec) { g_last_vec = vec ? 1 : 0; }
+
+}  // namespace zero
+
+using namespace zero;
+
+extern "C" {
+
+const char* zero_status_string(int status) {
+  switch (status) {
+    case ZERO_OK: return "ZERO_OK";
+    case ZERO_ERR_ARG: return "ZERO_ERR_ARG: invalid argument";
+    case ZERO_ERR_ALIGN: return "ZERO_ERR_ALIGN: misaligned pointer";
+    case ZERO_ERR_SIZE: return "ZERO_ERR_SIZE: inconsistent sizes";
+    case ZERO_ERR_HIP: return "ZERO_ERR_HIP: HIP runtime error";
+    case ZERO_ERR_STATE: return "ZERO_ERR_STATE: offload handle used out of order";
+    default: return "unknown zero_status";
+  }
+}
+
+const char* zero_last_error(void) { return g_last_error; }
+
+int zero_last_path_vectorized(void) { return g_last_vec; }
+
+int zero_adam_scalars_compute(const zero_adam_hparams* hp, zero_adam_scalars* out) {
+  Err e;
+  int st = adam_scalars(hp, out, e);
+  return st ? fail(st, e.msg) : ZERO_OK;
+}
+
+int zero_rank_weights(const int64_t* counts, int n_ranks, float* weights_out) {
+  Err e;
+  int st = rank_weights(counts, n_ranks, weights_out, e);
+  return st ? fail(st, e.msg) : ZERO_OK;
+}
+
+int zero_shard_layout(const int64_t* numels, int n_tensors, int n_shards, int64_t* psi,
+                      int64_t* psi_pad, int64_t* shard_numel) {
+  Err e;
+  int st = shard_layout(numels, n_tensors, n_shards, psi, psi_pad, shard_numel, e);
+  return st ? fail(st, e.msg) : ZERO_OK;
+}
+
+int zero_reduce_scatter(const uint16_t* const* rank_grads, const float* rank_weights, int n_ranks,
+                        int64_t numel, float* const* shards_out, int n_shards, int accumulate,
+                        void* stream) {
+  Err e;
+  int st = check_reduce_scatter(rank_grads, rank_weights, n_ranks, numel, shards_out, n_shards,
+                                accumulate, e);
+  if (st) return fail(st, e.msg);
+  if (numel == 0) return ZERO_OK;
+  RsParams p;
+  memset(&p, 0, sizeof p);
+  p.shard = numel / n_shards;
+  p.n_ranks = n_ranks;
+  bool vec = (p.shard % 8) == 0;
+  for (int r = 0; r < n_ranks; ++r) {
+    p.g[r] = rank_grads[r];
+    p.w[r] = rank_weights[r];
+    vec = vec && aligned16(rank_grads[r]);
+  }
+  for (int k = 0; k < n_shards; ++k) {
+    p.out[k] = shards_out[k];
+    vec = vec && aligned16(shards_out[k]);
+  }
+  set_path(vec);
+  return hip_status(launch_reduce_scatter(p, n_shards, accumulate != 0, vec,
+                                          static_cast<hipStream_t>(stream)),
+                    "zero_reduce_scatter");
+}
+
+int zero_adam_shard_step(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* bf16_out,
+                         const float* grad, int64_t n, const zero_adam_hparams* hp, void* stream) {
+  Err e;
+  int st = check_adam(master, exp_avg, exp_avg_sq, bf16_out, grad, n, hp, e);
+  if (st) return fail(st, e.msg);
+  if (n == 0) return ZERO_OK;
+  AdamParams a;
+  a.p = master;
+  a.m = exp_avg;
+  a.v = exp_avg_sq;
+  a.b = bf16_out;
+  a.g = grad;
+  a.n = n;
+  adam_scalars(hp, &a.s, e);
+  const bool vec = aligned16(master) && aligned16(exp_avg) && aligned16(exp_avg_sq) &&
+                   aligned16(grad) && (reinterpret_cast<uintptr_t>(bf16_out) & 7u) == 0;
+  set_path(vec);
+  return hip_status(launch_adam(a, vec, static_cast<hipStream_t>(stream)), "zero_adam_shard_step");
+}
+
+int zero_all_gather_layer(const void* const* shards, int n_shards, int64_t shard_bytes,
+                          void* full_view, void* stream) {
+  Err e;
+  int st = check_all_gather(shards, n_shards, shard_bytes, full_view, e);
+  if (st) return fail(st, e.msg);
+  if (shard_bytes == 0) return ZERO_OK;
+  GatherParams p;
+  memset(&p, 0, sizeof p);
+  p.dst = full_view;
+  p.shard_bytes = shard_bytes;
+  uintptr_t bits = reinterpret_cast<uintptr_t>(full_view) | static_cast<uintptr_t>(shard_bytes);
+  for (int k = 0; k < n_shards; ++k) {
+    p.src[k] = shards[k];
+    bits |= reinterpret_cast<uintptr_t>(shards[k]);
+  }
+  const int path = (bits & 15u) == 0 ? GATHER_V16 : (bits & 3u) == 0 ? GATHER_U32 : GATHER_U8;
+  set_path(path == GATHER_V16);
+  return hip_status(launch_gather(p, n_shards, path, static_cast<hipStream_t>(stream)),
+                    "zero_all_gather_layer");
+}
+
+}  // extern "C"
