@@ -2,17 +2,22 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one pass of the whole hot path over one batch of synthetic input:
-reduce-scatter of N=4 ranks' BF16 gradients into 4 FP32 owner shards (one
-launch), the fused Adam/AdamW update of each owner shard (4 launches), and the
-all-gather of the 4 BF16 working shards into the full view (one launch).  The
-default workload is one 7B-class transformer layer (d=4096, ffn=11008,
-202,375,168 parameters) with ranks weighted by token counts 4096/3072/4096/2048
-and AdamW (wd=0.1).  Inputs are resident in HBM before the timed region.
+A step is one pass of the whole hot path over one batch of synthetic input.
+The default workload is one 7B-class transformer layer (d=4096, ffn=11008,
+202,375,168 parameters, N=4 ranks weighted by token counts 4096/3072/4096/2048,
+AdamW wd=0.1): reduce-scatter of the 4 ranks' BF16 gradients into 4 FP32 owner
+shards (one launch), the fused Adam/AdamW update of each owner shard (4
+launches) and the all-gather of the 4 BF16 working shards into the full view
+(one launch).  Inputs are resident in HBM before the timed region.
+
+Other workloads (--workload): tiny_flat_1m, owner_share_8b_buckets (one
+owner's 2.0e9-parameter share in 64M buckets), zero3_chain_llama8b (34-unit
+gather/scatter chain of an 8B Llama-like model), offload_owner_8b_two_slots
+(host-offloaded gradient shard through two device slots).
 
 Prints ONE JSON line: params updated per second (value), the step time, the
 achieved algorithmic HBM bandwidth, the roofline entry of the dominant kernel
-(the Adam update) measured with HIP events on the launch stream, and the CPU
+measured with HIP events on the launch stream, and (default workload) the CPU
 oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -30,30 +35,33 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0          # MI355X published peak HBM3E bandwidth
 KERNEL_SRC = os.path.join(ROOT, "zero_sharded_optimizer_reduce_amd", "csrc", "kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adam_shard_step_layer7b_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
+METRIC = "params updated/sec per step and achieved HBM GB/s (% of MI355X peak), N=4"
 
-# algorithmic HBM bytes per parameter (N = 4 ranks)
+# algorithmic HBM bytes per parameter
 B_RS = lambda n: 2 * n + 4      # read N BF16 contributions, write one FP32 sum
+B_RS_ACC = lambda n: 2 * n + 8  # ... plus read the FP32 accumulator
 B_ADAM = 30                     # read g, p, m, v (16 B); write p, m, v (12 B) + BF16 (2 B)
 B_AG = 4                        # read and write one BF16 value
 
 
-def _kernel_hash() -> str:
+def kernel_source_hash() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def _traffic(launch_params: int):
-    """HBM bytes per Adam launch from the committed rocprofv3 counter summary,
-    or None if there is none or the kernel source changed since it was taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def _traffic(kernel: str, workload: str, launch_params: int):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None if there is none or the kernel source changed since."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
-        if ":" in line and not line.startswith("#"):
+    for line in open(path):
+        if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != _kernel_hash():
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
         return None
     try:
         if int(kv["params_per_launch"]) != launch_params:
@@ -63,13 +71,56 @@ def _traffic(launch_params: int):
         return None
 
 
-def _cpu_baseline(target_s: float):
-    """The oracle, as it stands, on 2^22-parameter slices of the same workload
-    (reduce-scatter of 4 count-weighted BF16 ranks, AdamW, BF16 pack, gather),
-    repeated until target_s seconds of CPU work.  numpy's element-wise ufuncs
-    run on one thread."""
-    import numpy as np
+def _roofline(kernel, workload, ms, params):
+    achieved = B_ADAM * params / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": _traffic(kernel, workload, params),
+            "kernel": kernel, "algorithmic_bytes_per_launch": B_ADAM * params}
 
+
+def _mean(xs):
+    return float(sum(xs) / max(1, len(xs)))
+
+
+class Timer:
+    """HIP events on the launch stream (the current torch stream, which every
+    library call here is given)."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+        self.spans = {}
+
+    def ev(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        return e
+
+    def span(self, name, a, b):
+        self.spans.setdefault(name, []).append((a, b))
+
+    def ms(self, name):
+        return _mean([a.elapsed_time(b) for a, b in self.spans.get(name, [])])
+
+    def total_ms(self, name):
+        return float(sum(a.elapsed_time(b) for a, b in self.spans.get(name, [])))
+
+
+def _base(workload_desc, value, ms_step, args, extra_cfg=None):
+    cfg = {"workload": workload_desc}
+    cfg.update(extra_cfg or {})
+    return {"metric": METRIC, "value": value, "unit": "params/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": cfg}
+
+
+# --------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(target_s: float):
+    """The oracle, as it stands, on 2^22-parameter slices of the 7B-class layer
+    workload (reduce-scatter of 4 count-weighted BF16 ranks, AdamW, BF16 pack,
+    gather), repeated until target_s seconds of CPU work.  numpy's element-wise
+    ufuncs run on one thread."""
     import oracle
     import synthetic as S
     from synthetic.workloads import LAYER_7B as wl
@@ -83,15 +134,14 @@ def _cpu_baseline(target_s: float):
     done, reps = 0, 0
     t0 = time.perf_counter()
     while True:
-        outs, view = oracle.sharded_step(grads, w, [p[k * s:(k + 1) * s] for k in range(n)],
-                                         [m[k * s:(k + 1) * s] for k in range(n)],
-                                         [v[k * s:(k + 1) * s] for k in range(n)], sc)
+        oracle.sharded_step(grads, w, [p[k * s:(k + 1) * s] for k in range(n)],
+                            [m[k * s:(k + 1) * s] for k in range(n)],
+                            [v[k * s:(k + 1) * s] for k in range(n)], sc)
         done += chunk
         reps += 1
         el = time.perf_counter() - t0
         if el >= target_s:
             break
-    del outs, view
     return {"value": done / el, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": (f"oracle sharded step on a 2^22-param slice of the 7B-class layer "
                        f"(4 count-weighted BF16 ranks, AdamW, BF16 pack, all-gather), "
@@ -99,103 +149,349 @@ def _cpu_baseline(target_s: float):
                        f"host has {os.cpu_count()} CPUs")}
 
 
-def run_layer7b(args):
-    import numpy as np
+# --------------------------------------------------------------------------- flat units
+def run_flat(args, wl, numels, grad_scales=None, counts=None, steps_are_adam_t=True):
     import torch
 
     import synthetic as S
-    from synthetic.workloads import LAYER_7B as wl
     import zero_sharded_optimizer_reduce_amd as z
     from zero_sharded_optimizer_reduce_amd.drivers import ShardedStep
 
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     n = wl.n_ranks
-    st = ShardedStep(S.unit_numels(S.workloads.layer_7b_tensors()), n, device=dev)
+    st = ShardedStep(numels, n, device=dev)
     gen = S.DeviceGen(wl.seed)
     st.load_master(gen.normal_(torch.empty(st.psi_pad, device=dev), wl.master_sigma, 0))
-    scales = S.rank_scales(wl.seed, n)
+    scales = grad_scales or [1.0] * n
     grads = [torch.empty(st.psi_pad, dtype=torch.bfloat16, device=dev) for _ in range(n)]
     tmp = torch.empty(st.psi_pad, dtype=torch.float32, device=dev)
     for r in range(n):
         gen.bf16_normal_(grads[r], wl.grad_sigma, 1, r, scale=scales[r], tmp=tmp)
     del tmp
-    w = z.zero_rank_weights(wl.extra["token_counts"], n)
-    stream = torch.cuda.current_stream()
+    w = z.zero_rank_weights(counts, n)
+    T = Timer()
     torch.cuda.synchronize()
-
     t = 0
     for _ in range(args.warmup):
         t += 1
         st.step(grads, w, wl.hparams(step=t))
     torch.cuda.synchronize()
-
-    E = lambda: torch.cuda.Event(enable_timing=True)
-    ev = [[E() for _ in range(2 + 2 * n + 2)] for _ in range(args.steps)]
-    start, stop = E(), E()
-    torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
+    start = T.ev()
+    for _ in range(args.steps):
         t += 1
         hp = wl.hparams(step=t)
-        e = ev[i]
-        e[0].record(stream)
+        a = T.ev()
         st.reduce_scatter(grads, w)
-        e[1].record(stream)
+        b = T.ev()
+        T.span("rs", a, b)
         for k in range(n):
-            e[2 + 2 * k].record(stream)
+            a = T.ev()
             z.zero_adam_shard_step(st.master[k], st.exp_avg[k], st.exp_avg_sq[k], st.bf16[k], st.grad[k], hp)
-            e[3 + 2 * k].record(stream)
-        e[2 + 2 * n].record(stream)
+            b = T.ev()
+            T.span("adam", a, b)
+        a = T.ev()
         st.all_gather()
-        e[3 + 2 * n].record(stream)
-    stop.record(stream)
+        b = T.ev()
+        T.span("ag", a, b)
+    stop = T.ev()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
-    total_ms = start.elapsed_time(stop)
-    ms_step = total_ms / args.steps
-    rs_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    adam_ms = float(np.mean([e[2 + 2 * k].elapsed_time(e[3 + 2 * k]) for e in ev for k in range(n)]))
-    ag_ms = float(np.mean([e[2 + 2 * n].elapsed_time(e[3 + 2 * n]) for e in ev]))
-
-    psi, S_ = st.psi, st.shard
-    step_bytes = (B_RS(n) + B_ADAM + B_AG) * st.psi_pad
-    adam_bytes = B_ADAM * S_
-    achieved = adam_bytes / (adam_ms * 1e-3) / 1e9
-    traffic = _traffic(S_)
-    out = {
-        "metric": "params updated/sec per step and achieved HBM GB/s (% of MI355X peak), N=4",
-        "value": psi / (ms_step * 1e-3),
-        "unit": "params/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": wl.description, "params": psi, "n_ranks": n,
-                   "storage": "bf16 grads and working weights, fp32 master/m/v",
-                   "step": "reduce-scatter + 4 owner Adam updates + all-gather"},
+    ms_step = start.elapsed_time(stop) / args.steps
+    pad = st.psi_pad
+    step_bytes = (B_RS(n) + B_ADAM + B_AG) * pad
+    rs_ms, adam_ms, ag_ms = T.ms("rs"), T.ms("adam"), T.ms("ag")
+    out = _base(wl.description, st.psi / (ms_step * 1e-3), ms_step, args,
+                {"params": st.psi, "n_ranks": n, "storage": "bf16 grads and working weights, fp32 master/m/v",
+                 "step": "reduce-scatter + 4 owner Adam updates + all-gather"})
+    out.update({
         "hbm_gbs_algorithmic": step_bytes / (ms_step * 1e-3) / 1e9,
         "hbm_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "wall_s_timed": wall,
         "kernels": {
-            "reduce_scatter": {"ms": rs_ms, "bytes": B_RS(n) * st.psi_pad,
-                               "gbs": B_RS(n) * st.psi_pad / (rs_ms * 1e-3) / 1e9},
-            "adam_shard_step": {"ms": adam_ms, "bytes": adam_bytes, "gbs": achieved},
-            "all_gather": {"ms": ag_ms, "bytes": B_AG * st.psi_pad,
-                           "gbs": B_AG * st.psi_pad / (ag_ms * 1e-3) / 1e9},
+            "reduce_scatter": {"ms": rs_ms, "bytes": B_RS(n) * pad, "gbs": B_RS(n) * pad / (rs_ms * 1e-3) / 1e9},
+            "adam_shard_step": {"ms": adam_ms, "bytes": B_ADAM * st.shard,
+                                "gbs": B_ADAM * st.shard / (adam_ms * 1e-3) / 1e9},
+            "all_gather": {"ms": ag_ms, "bytes": B_AG * pad, "gbs": B_AG * pad / (ag_ms * 1e-3) / 1e9},
         },
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": traffic, "kernel": "adam_shard_step",
-                     "algorithmic_bytes_per_launch": adam_bytes},
-    }
+        "roofline": _roofline("adam_shard_step", wl.name, adam_ms, st.shard),
+    })
     return out
+
+
+def run_layer7b(args):
+    import synthetic as S
+    from synthetic.workloads import LAYER_7B as wl
+    return run_flat(args, wl, S.unit_numels(S.workloads.layer_7b_tensors()),
+                    grad_scales=S.rank_scales(wl.seed, wl.n_ranks), counts=wl.extra["token_counts"])
+
+
+def run_tiny(args):
+    from synthetic.workloads import TINY as wl
+    return run_flat(args, wl, [wl.psi])
+
+
+# --------------------------------------------------------------------------- owner share, buckets
+def run_owner_share(args):
+    import torch
+
+    import synthetic as S
+    from synthetic import fill
+    from synthetic.workloads import OWNER_8B as wl
+    import zero_sharded_optimizer_reduce_amd as z
+    from zero_sharded_optimizer_reduce_amd.drivers import BucketedOwnerStep
+
+    n = wl.n_ranks
+    st = BucketedOwnerStep(wl.psi, n, wl.extra["bucket"], device="cuda")
+    gen = S.DeviceGen(wl.seed)
+    tmp = torch.empty(wl.extra["bucket"], dtype=torch.float32, device="cuda")
+    fill.fill_owner_share(gen, wl, st.master, st.exp_avg, st.exp_avg_sq, st.contrib, tmp)
+    del tmp
+    w = z.zero_rank_weights(None, n)
+    T = Timer()
+    torch.cuda.synchronize()
+    t = wl.step0 - 1
+    for _ in range(args.warmup):
+        t += 1
+        st.step(w, wl.hparams(step=t))
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    start = T.ev()
+    for _ in range(args.steps):
+        t += 1
+        hp = wl.hparams(step=t)
+        for b, (lo, hi) in enumerate(st.bounds):
+            g = st.grad_bucket[: hi - lo]
+            a = T.ev()
+            z.zero_reduce_scatter([c[lo:hi] for c in st.contrib], w, [g])
+            m = T.ev()
+            z.zero_adam_shard_step(st.master[lo:hi], st.exp_avg[lo:hi], st.exp_avg_sq[lo:hi], st.bf16[lo:hi], g, hp)
+            e = T.ev()
+            if hi - lo == st.bucket:
+                T.span("rs", a, m)
+                T.span("adam", m, e)
+    stop = T.ev()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    ms_step = start.elapsed_time(stop) / args.steps
+    step_bytes = (B_RS(n) + B_ADAM) * wl.psi
+    rs_ms, adam_ms = T.ms("rs"), T.ms("adam")
+    B = st.bucket
+    out = _base(wl.description, wl.psi / (ms_step * 1e-3), ms_step, args,
+                {"params": wl.psi, "n_ranks": n, "bucket": B, "buckets": len(st.bounds),
+                 "step": "per bucket: reduce 4 pre-sliced contributions + owner Adam update"})
+    out.update({
+        "hbm_gbs_algorithmic": step_bytes / (ms_step * 1e-3) / 1e9,
+        "hbm_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "wall_s_timed": wall,
+        "kernels": {"reduce_scatter": {"ms": rs_ms, "bytes": B_RS(n) * B, "gbs": B_RS(n) * B / (rs_ms * 1e-3) / 1e9},
+                    "adam_shard_step": {"ms": adam_ms, "bytes": B_ADAM * B, "gbs": B_ADAM * B / (adam_ms * 1e-3) / 1e9}},
+        "roofline": _roofline("adam_shard_step", wl.name, adam_ms, B),
+    })
+    return out
+
+
+# --------------------------------------------------------------------------- ZeRO-3 chain
+def run_chain(args):
+    import torch
+
+    import synthetic as S
+    from synthetic import fill
+    from synthetic.workloads import CHAIN_8B as wl
+    import zero_sharded_optimizer_reduce_amd as z
+    from zero_sharded_optimizer_reduce_amd.drivers import Zero3Chain
+
+    n = wl.n_ranks
+    torch.cuda.reset_peak_memory_stats()
+    ch = Zero3Chain(wl.extra["units"], n, device="cuda")
+    gen = S.DeviceGen(wl.seed)
+    for k in range(n):
+        fill.fill_normal_pieces(gen, ch.master[k], wl.master_sigma, fill.K_MASTER + 100 * k)
+        for lo, hi in fill.pieces(ch.owner_numel):
+            ch.bf16[k][lo:hi].copy_(ch.master[k][lo:hi])
+    tmp = torch.empty(ch.max_pad, dtype=torch.float32, device="cuda")
+    w = z.zero_rank_weights(None, n)
+    T = Timer()
+    U = len(ch.units)
+
+    def step(t, timed):
+        hp = wl.hparams(step=t)
+        for u in range(U):                      # forward: gather, use, release
+            a = T.ev() if timed else None
+            ch.forward_unit(u)
+            if timed:
+                T.span("ag" if u not in (0, U - 1) else "ag_edge", a, T.ev())
+        for u in reversed(range(U)):            # backward
+            pad = ch.units[u][2]
+            fill.chain_unit_grads(gen, wl, u, ch.grads, pad, tmp)   # producer, not timed
+            a = T.ev() if timed else None
+            ch.backward_unit(u, w, hp)
+            if timed:
+                T.span("bwd" if u not in (0, U - 1) else "bwd_edge", a, T.ev())
+
+    torch.cuda.synchronize()
+    t = 0
+    for _ in range(args.warmup):
+        t += 1
+        step(t, False)
+    torch.cuda.synchronize()
+    # per-kernel durations on one representative layer unit (timed separately)
+    t_wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        t += 1
+        step(t, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    fwd_ms = (T.total_ms("ag") + T.total_ms("ag_edge")) / args.steps
+    bwd_ms = (T.total_ms("bwd") + T.total_ms("bwd_edge")) / args.steps
+    ms_step = fwd_ms + bwd_ms
+    psi_pad = sum(u[2] for u in ch.units)
+    step_bytes = (B_RS(n) + B_ADAM + B_AG) * psi_pad
+    # kernel-level timing of one layer unit
+    lay = 1
+    pad, s = ch.units[lay][2], ch.units[lay][3]
+    fill.chain_unit_grads(gen, wl, lay, ch.grads, pad, tmp)
+    hp = wl.hparams(step=t + 1)
+    for _ in range(3):
+        a = T.ev()
+        z.zero_reduce_scatter([g[:pad] for g in ch.grads], w, [g[:s] for g in ch.grad_shards])
+        b = T.ev()
+        T.span("k_rs", a, b)
+        for k in range(n):
+            p, m, v, bb = (x[ch.offsets[lay]:ch.offsets[lay] + s] for x in
+                           (ch.master[k], ch.exp_avg[k], ch.exp_avg_sq[k], ch.bf16[k]))
+            a = T.ev()
+            z.zero_adam_shard_step(p, m, v, bb, ch.grad_shards[k][:s], hp)
+            T.span("k_adam", a, T.ev())
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated()
+    adam_ms = T.ms("k_adam")
+    persistent = sum(x.numel() * x.element_size() for x in ch.master + ch.exp_avg + ch.exp_avg_sq + ch.bf16)
+    out = _base(wl.description, wl.psi / (ms_step * 1e-3), ms_step, args,
+                {"params": wl.psi, "n_ranks": n, "units": U,
+                 "step": "forward: 34 all-gathers into a released view; backward (reverse): "
+                         "reduce-scatter + 4 owner Adam updates per unit; gradient generation excluded"})
+    out.update({
+        "hbm_gbs_algorithmic": step_bytes / (ms_step * 1e-3) / 1e9,
+        "hbm_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "forward_ms": fwd_ms, "backward_ms": bwd_ms, "wall_s_timed_incl_generation": wall,
+        "memory": {"persistent_bytes_all_owners": persistent,
+                   "ledger_zero3_bytes_all_owners": 16 * wl.psi,
+                   "peak_allocated_bytes": peak},
+        "kernels": {"reduce_scatter_layer": {"ms": T.ms("k_rs"), "bytes": B_RS(n) * pad},
+                    "adam_shard_step_layer": {"ms": adam_ms, "bytes": B_ADAM * s,
+                                              "gbs": B_ADAM * s / (adam_ms * 1e-3) / 1e9}},
+        "roofline": _roofline("adam_shard_step", wl.name, adam_ms, s),
+    })
+    return out
+
+
+# --------------------------------------------------------------------------- offload
+def _pinned_copy_rates(nbytes):
+    """Pinned host <-> device hipMemcpyAsync rates in this process: H2D alone,
+    D2H alone, and both at once on two streams (GB/s)."""
+    import torch
+    h = torch.empty(nbytes // 4, dtype=torch.float32, pin_memory=True)
+    h2 = torch.empty(nbytes // 4, dtype=torch.float32, pin_memory=True)
+    d = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    d2 = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    res = {}
+    for _ in range(2):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(s1):
+            d.copy_(h, non_blocking=True)
+        torch.cuda.synchronize()
+        res["h2d_gbs"] = nbytes / (time.perf_counter() - t0) / 1e9
+        t0 = time.perf_counter()
+        with torch.cuda.stream(s1):
+            h.copy_(d, non_blocking=True)
+        torch.cuda.synchronize()
+        res["d2h_gbs"] = nbytes / (time.perf_counter() - t0) / 1e9
+        t0 = time.perf_counter()
+        with torch.cuda.stream(s1):
+            d.copy_(h, non_blocking=True)
+        with torch.cuda.stream(s2):
+            h2.copy_(d2, non_blocking=True)
+        torch.cuda.synchronize()
+        res["bidir_gbs"] = 2 * nbytes / (time.perf_counter() - t0) / 1e9
+    return res
+
+
+def run_offload(args):
+    import torch
+
+    import synthetic as S
+    from synthetic import fill
+    from synthetic.workloads import OFFLOAD_8B as wl
+    import zero_sharded_optimizer_reduce_amd as z
+    from zero_sharded_optimizer_reduce_amd.drivers import OffloadStep
+
+    n, M, C = wl.n_ranks, wl.extra["micro_batches"], wl.extra["chunk"]
+    st = OffloadStep(wl.psi, n, C, device="cuda")
+    gen = S.DeviceGen(wl.seed)
+    tmp = torch.empty(C, dtype=torch.float32, device="cuda")
+    fill.fill_normal_pieces(gen, st.master, wl.master_sigma, fill.K_MASTER)
+    # producer: copies one of P pre-drawn contribution sets into the slot, as a
+    # backward pass would write its gradient chunk
+    P = 4
+    pool = [torch.empty(n * C, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    for i, pbuf in enumerate(pool):
+        fill.offload_contrib(gen, wl, 100 + i, 0, [pbuf[r * C:(r + 1) * C] for r in range(n)], tmp)
+    del tmp
+    w = [1.0 / (n * M)] * n
+
+    def produce(mb, c, views):
+        src = pool[(mb * 7 + c) % P]
+        for r, vw in enumerate(views):
+            vw.copy_(src[r * C: r * C + vw.numel()])
+
+    torch.cuda.synchronize()
+    t = 0
+    for _ in range(args.warmup):
+        t += 1
+        st.step(produce, M, w, wl.hparams(step=t))
+        st.sync()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(args.steps):
+        t += 1
+        t0 = time.perf_counter()
+        st.step(produce, M, w, wl.hparams(step=t))
+        st.sync()
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    ms_step = 1e3 * _mean(times)
+    link_bytes = 4 * wl.psi * (M + (M - 1) + 1)     # D2H every mb, H2D from mb 2, H2D stream-back
+    rates = _pinned_copy_rates(1 << 30)
+    ideal_s = (4 * wl.psi * M) / (rates["d2h_gbs"] * 1e9)
+    out = _base(wl.description, wl.psi / (ms_step * 1e-3), ms_step, args,
+                {"params": wl.psi, "n_ranks": n, "chunk": C, "micro_batches": M,
+                 "step": "M x chunks: reduce into slot c%2 (+H2D of the host chunk from mb 2) and D2H; "
+                         "then per chunk H2D + owner Adam"})
+    out.update({
+        "bound": "host link (PCIe)",
+        "link_gbs": link_bytes / (ms_step * 1e-3) / 1e9,
+        "link_bytes_per_step": link_bytes,
+        "pinned_copy_rates_same_process": rates,
+        "overlap_bound_ms": 1e3 * max(ideal_s, (4 * wl.psi * M) / (rates["h2d_gbs"] * 1e9)),
+        "roofline": {"bound": "link", "achieved": link_bytes / (ms_step * 1e-3) / 1e9,
+                     "peak": rates["bidir_gbs"], "unit": "GB/s",
+                     "frac": (link_bytes / (ms_step * 1e-3) / 1e9) / rates["bidir_gbs"],
+                     "traffic": None, "kernel": "pinned copies (both directions)"},
+    })
+    st.engine.close()
+    return out
+
+
+RUNNERS = {
+    "layer7b_weighted_adamw": run_layer7b,
+    "tiny_flat_1m": run_tiny,
+    "owner_share_8b_buckets": run_owner_share,
+    "zero3_chain_llama8b": run_chain,
+    "offload_owner_8b_two_slots": run_offload,
+}
 
 
 def main():
@@ -203,7 +499,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="layer7b_weighted_adamw")
+    ap.add_argument("--workload", default="layer7b_weighted_adamw", choices=sorted(RUNNERS))
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -215,16 +511,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    torch.cuda.set_device(0)
     from zero_sharded_optimizer_reduce_amd import _lib
     if not os.path.exists(_lib.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
-    if args.workload != "layer7b_weighted_adamw":
-        print(f"unknown workload {args.workload}", file=sys.stderr)
-        sys.exit(2)
-    out = run_layer7b(args)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = _cpu_baseline(args.cpu_baseline_seconds)
+    out = RUNNERS[args.workload](args)
+    if args.workload == "layer7b_weighted_adamw" and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_baseline_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -108,3 +108,32 @@ def test_layer7b_three_adamw_steps():
             assert_state_close(gp[a:a + width], gm[a:a + width], gv[a:a + width], gb[a:a + width], ref,
                                f"window {a} step {t}")
             cpu_p[j], cpu_m[j], cpu_v[j] = ref[0], ref[1], ref[2]
+
+
+def test_resume_from_saved_state_is_bit_exact():
+    # 3 steps in one go equal 2 steps, a save of the owners' state to host
+    # memory, a reload into fresh buffers and 1 more step
+    n, psi = 4, 4 * 256 * 37 + 1000
+    hp = lambda t: dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1, step=t)
+    grads = [[bf16_to_dev(g) for g in S.host_rank_grads(900 + t, n, oracle.shard_layout([psi], n)[1])]
+             for t in range(3)]
+    p0 = torch.from_numpy(S.host_state(901, oracle.shard_layout([psi], n)[1], 0.02)[0]).cuda()
+    w = oracle.weights_from_counts([3, 1, 4, 1])
+    a = ShardedStep([psi], n)
+    a.load_master(p0)
+    for t in range(3):
+        a.step(grads[t], w, hp(t + 1))
+    b = ShardedStep([psi], n)
+    b.load_master(p0)
+    for t in range(2):
+        b.step(grads[t], w, hp(t + 1))
+    saved = [[x.cpu().clone() for x in bufs] for bufs in (b.master, b.exp_avg, b.exp_avg_sq)]
+    c = ShardedStep([psi], n)
+    for bufs, host in zip((c.master, c.exp_avg, c.exp_avg_sq), saved):
+        for dst, src in zip(bufs, host):
+            dst.copy_(src)
+    c.step(grads[2], w, hp(3))
+    torch.cuda.synchronize()
+    for xa, xc in zip(a.master + a.exp_avg + a.exp_avg_sq, c.master + c.exp_avg + c.exp_avg_sq):
+        assert np.array_equal(f32_to_host(xa).view(np.uint32), f32_to_host(xc).view(np.uint32))
+    assert np.array_equal(bf16_to_host(a.view), bf16_to_host(c.view))
