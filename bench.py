@@ -216,6 +216,28 @@ def run_flat(args, wl, numels, grad_scales=None, counts=None, steps_are_adam_t=T
         },
         "roofline": _roofline("adam_shard_step", wl.name, adam_ms, st.shard),
     })
+    # the same step with the fused reduce-scatter + update kernel (one launch
+    # for all owners, reduced gradient kept in registers) and the all-gather
+    torch.cuda.synchronize()
+    start = T.ev()
+    for _ in range(args.steps):
+        t += 1
+        hp = wl.hparams(step=t)
+        a = T.ev()
+        z.zero_reduce_scatter_adam(grads, w, st.master, st.exp_avg, st.exp_avg_sq, st.bf16, hp)
+        T.span("fused", a, T.ev())
+        st.all_gather()
+    stop = T.ev()
+    torch.cuda.synchronize()
+    f_ms = start.elapsed_time(stop) / args.steps
+    fk = T.ms("fused")
+    out["fused_variant"] = {
+        "ms_per_step": f_ms, "value": st.psi / (f_ms * 1e-3),
+        "step": "fused reduce-scatter + 4 owner updates (one launch) + all-gather, 38 B/param",
+        "fused_kernel": {"ms": fk, "bytes": (2 * n + 26) * pad,
+                         "gbs": (2 * n + 26) * pad / (fk * 1e-3) / 1e9},
+        "hbm_gbs_algorithmic": (2 * n + 26 + B_AG) * pad / (f_ms * 1e-3) / 1e9,
+    }
     return out
 
 
@@ -485,12 +507,36 @@ def run_offload(args):
     return out
 
 
+def run_copy_calibration(args):
+    """A plain copy kernel of known size for scaling the HBM byte counters:
+    zero_all_gather_layer with one 1 GiB shard (reads 1 GiB, writes 1 GiB)."""
+    import torch
+
+    import zero_sharded_optimizer_reduce_amd as z
+
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    T = Timer()
+    for _ in range(args.warmup):
+        z.zero_all_gather_layer([src], dst)
+    for _ in range(args.steps):
+        a = T.ev()
+        z.zero_all_gather_layer([src], dst)
+        T.span("copy", a, T.ev())
+    torch.cuda.synchronize()
+    ms = T.ms("copy")
+    return {"calibration": "copy", "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
+            "ms": ms, "gbs": 2 * nbytes / (ms * 1e-3) / 1e9, "launches": args.steps + args.warmup}
+
+
 RUNNERS = {
     "layer7b_weighted_adamw": run_layer7b,
     "tiny_flat_1m": run_tiny,
     "owner_share_8b_buckets": run_owner_share,
     "zero3_chain_llama8b": run_chain,
     "offload_owner_8b_two_slots": run_offload,
+    "copy_calibration": run_copy_calibration,
 }
 
 

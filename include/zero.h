@@ -143,6 +143,27 @@ int zero_reduce_scatter(const uint16_t* const* rank_grads, const float* rank_wei
 int zero_adam_shard_step(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* bf16_out,
                          const float* grad, int64_t n, const zero_adam_hparams* hp, void* stream);
 
+/* Reduce-scatter and owner update in one pass ([blog] 三级分片, ZeRO-1: the
+ * optimizer step sits between the reduce-scatter and the all-gather).  For
+ * every owner k it computes exactly zero_reduce_scatter's shard k (without
+ * storing it unless grad_out is given) and applies zero_adam_shard_step's
+ * update to owner k's state with it, so the results are bit-identical to the
+ * two calls in sequence, with 8 fewer bytes of HBM traffic per parameter.
+ *
+ *   rank_grads, rank_weights, n_ranks, numel, n_shards: as zero_reduce_scatter.
+ *   master, exp_avg, exp_avg_sq  host arrays of n_shards device pointers to
+ *                FP32 state of numel/n_shards elements each (updated in place).
+ *   bf16_out     host array of n_shards device pointers to BF16 working shards.
+ *   grad_out     NULL, or a host array of n_shards device pointers to FP32
+ *                buffers that receive the reduced gradient shards.
+ * Errors: as zero_reduce_scatter and zero_adam_shard_step; every output must
+ * be disjoint from every other buffer. */
+int zero_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* rank_weights,
+                             int n_ranks, int64_t numel, int n_shards, float* const* master,
+                             float* const* exp_avg, float* const* exp_avg_sq,
+                             uint16_t* const* bf16_out, float* const* grad_out,
+                             const zero_adam_hparams* hp, void* stream);
+
 /* All-gather into a temporary full view ([slide] note 原 N47 and beat b2;
  * [essay] ZeRO-3 的一次完整计算; [blog] 三级分片, ZeRO-3): the owners'
  * shards, concatenated in owner order, form the full per-layer view.

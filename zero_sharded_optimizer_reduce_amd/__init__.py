@@ -18,5 +18,6 @@ from .api import (  # noqa: F401
     zero_offload_sync,
     zero_rank_weights,
     zero_reduce_scatter,
+    zero_reduce_scatter_adam,
     zero_shard_layout,
 )

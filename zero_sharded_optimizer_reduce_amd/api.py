@@ -113,6 +113,43 @@ def zero_adam_shard_step(master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq
     check(load().zero_adam_shard_step(*ptrs, n, C.byref(h), _stream(stream)), "zero_adam_shard_step")
 
 
+def zero_reduce_scatter_adam(rank_grads: Sequence[torch.Tensor], rank_weights, master, exp_avg, exp_avg_sq,
+                             bf16_out, hp, grad_out=None, stream=None) -> None:
+    """Fused reduce-scatter + owner Adam update: for each owner k, the reduced
+    shard k of the rank contributions updates (master[k], exp_avg[k],
+    exp_avg_sq[k]) and writes bf16_out[k]; grad_out (optional list) receives
+    the reduced shards.  Bit-identical to zero_reduce_scatter followed by
+    zero_adam_shard_step on every owner."""
+    n_ranks, n_shards = len(rank_grads), len(master)
+    if n_ranks < 1 or n_shards < 1:
+        raise ValueError("zero_reduce_scatter_adam: need at least one rank and one owner")
+    numel = rank_grads[0].numel()
+    gp = [_dev(g, f"rank_grads[{r}]", _BF16_LIKE) for r, g in enumerate(rank_grads)]
+    if any(g.numel() != numel for g in rank_grads):
+        raise ValueError("zero_reduce_scatter_adam: rank contributions differ in size")
+    if numel % n_shards:
+        raise ValueError("zero_reduce_scatter_adam: numel not divisible by the number of owners")
+    s = numel // n_shards
+    tables = []
+    for name, ts, dt in (("master", master, (torch.float32,)), ("exp_avg", exp_avg, (torch.float32,)),
+                         ("exp_avg_sq", exp_avg_sq, (torch.float32,)), ("bf16_out", bf16_out, _BF16_LIKE)):
+        if len(ts) != n_shards or any(t.numel() != s for t in ts):
+            raise ValueError(f"zero_reduce_scatter_adam: {name} needs {n_shards} tensors of {s} elements")
+        tables.append(_ptrs([_dev(t, f"{name}[{k}]", dt) for k, t in enumerate(ts)]))
+    go = None
+    if grad_out is not None:
+        if len(grad_out) != n_shards or any(t.numel() != s for t in grad_out):
+            raise ValueError("zero_reduce_scatter_adam: grad_out needs one tensor per owner")
+        go = _ptrs([_dev(t, f"grad_out[{k}]", (torch.float32,)) for k, t in enumerate(grad_out)])
+    w = np.ascontiguousarray(np.asarray(rank_weights, dtype=np.float32))
+    if w.size != n_ranks:
+        raise ValueError("zero_reduce_scatter_adam: one weight per rank")
+    h = hparams(hp)
+    check(load().zero_reduce_scatter_adam(_ptrs(gp), w.ctypes.data_as(_lib.FP), n_ranks, numel, n_shards,
+                                          *tables, go, C.byref(h), _stream(stream)),
+          "zero_reduce_scatter_adam")
+
+
 def zero_all_gather_layer(shards: Sequence[torch.Tensor], full_view: torch.Tensor, stream=None) -> None:
     """full_view = concatenation of the shards' bytes in owner order."""
     n = len(shards)

@@ -28,6 +28,19 @@ struct AdamParams {
   zero_adam_scalars s;
 };
 
+struct FusedParams {
+  const uint16_t* g[ZERO_MAX_RANKS];  // rank contributions, n_shards*shard BF16 each
+  float w[ZERO_MAX_RANKS];
+  float* p[ZERO_MAX_RANKS];           // per owner: master, m, v (FP32), working shard (BF16)
+  float* m[ZERO_MAX_RANKS];
+  float* v[ZERO_MAX_RANKS];
+  uint16_t* b[ZERO_MAX_RANKS];
+  float* gout[ZERO_MAX_RANKS];        // per owner: reduced gradient out, or all NULL
+  int64_t shard;
+  int n_ranks;
+  zero_adam_scalars s;
+};
+
 struct GatherParams {
   const void* src[ZERO_MAX_RANKS];
   void* dst;
@@ -35,11 +48,16 @@ struct GatherParams {
 };
 
 // Each launcher enqueues on `stream` and returns hipSuccess or the launch
-// error.  `vec` selects the 128-bit path; the caller has checked that every
-// pointer and per-shard offset it uses is 16-byte aligned.
+// error.  `vec` selects the vector path; the caller has checked its alignment
+// conditions: reduce-scatter and fused: shard % 4 == 0, BF16 contribution and
+// working-shard pointers 8-byte aligned, FP32 pointers 16-byte aligned;
+// Adam: n % 4 tail handled in-kernel, FP32 pointers 16-byte and the BF16
+// output 8-byte aligned.
 hipError_t launch_reduce_scatter(const RsParams& p, int n_shards, bool accumulate, bool vec,
                                  hipStream_t stream);
 hipError_t launch_adam(const AdamParams& p, bool vec, hipStream_t stream);
+hipError_t launch_fused(const FusedParams& p, int n_shards, bool write_grad, bool vec,
+                        hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, int n_shards, int path, hipStream_t stream);
 
 // Fill n 32-bit words with `value` (used to poison released staging buffers

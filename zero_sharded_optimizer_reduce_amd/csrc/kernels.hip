@@ -56,58 +56,57 @@ __device__ __forceinline__ void st_nt(T v, T* p) { __builtin_nontemporal_store(v
 // element-wise and never mixed with other parameters; the owner receives only
 // its slice (slide "分担数据，与分担保存责任，是两个动作", note 原 N48).
 //
-// Vector path: one 16-byte load per rank gives 8 BF16 values; the 8 FP32
-// results leave as two 16-byte stores.  U vectors per lane per iteration keep
-// N*U loads in flight before the first use.
+// Vector path: each lane reduces 4 consecutive elements: one 8-byte BF16 load
+// per rank, one 16-byte FP32 store, so every load and store instruction of a
+// wave covers one contiguous span (16-byte loads with two strided 16-byte
+// stores measured 5% slower: the stores then cover half lines).  U vectors
+// per lane keep N*U loads in flight before the first use.
+
+// The 4 reduced values of one lane; x[r] holds rank r's 4 BF16 values.
+template <int NMAX>
+__device__ __forceinline__ f32x4 reduce4(const u32x2 (&x)[NMAX], int n, const float* w) {
+  const float w0 = w[0];
+  float a0 = w0 * bf16_lo(x[0].x), a1 = w0 * bf16_hi(x[0].x);
+  float a2 = w0 * bf16_lo(x[0].y), a3 = w0 * bf16_hi(x[0].y);
+#pragma unroll
+  for (int r = 1; r < NMAX; ++r) {
+    if (r < n) {
+      const float wr = w[r];
+      a0 = a0 + wr * bf16_lo(x[r].x);
+      a1 = a1 + wr * bf16_hi(x[r].x);
+      a2 = a2 + wr * bf16_lo(x[r].y);
+      a3 = a3 + wr * bf16_hi(x[r].y);
+    }
+  }
+  return f32x4{a0, a1, a2, a3};
+}
+
 template <int N, bool ACC, int U>
 __global__ __launch_bounds__(kBlock) void rs_vec_kernel(RsParams p) {
   constexpr int NMAX = N > 0 ? N : ZERO_MAX_RANKS;
   const int n = N > 0 ? N : p.n_ranks;
   const int k = blockIdx.y;
-  const int64_t nvec = p.shard >> 3;
+  const int64_t nvec = p.shard >> 2;
   const int64_t off = static_cast<int64_t>(k) * nvec;
   f32x4* __restrict__ out = reinterpret_cast<f32x4*>(p.out[k]);
   const int64_t step = static_cast<int64_t>(gridDim.x) * kBlock * U;
   for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock * U + threadIdx.x; base < nvec;
        base += step) {
-    u32x4 x[U][NMAX];
+    u32x2 x[U][NMAX];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = base + u * kBlock;
 #pragma unroll
       for (int r = 0; r < NMAX; ++r)
-        if (r < n && i < nvec) x[u][r] = ld_nt(reinterpret_cast<const u32x4*>(p.g[r]) + off + i);
+        if (r < n && i < nvec) x[u][r] = ld_nt(reinterpret_cast<const u32x2*>(p.g[r]) + off + i);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = base + u * kBlock;
       if (i >= nvec) break;
-      float a[8];
-      const float w0 = p.w[0];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        a[2 * q] = w0 * bf16_lo(x[u][0][q]);
-        a[2 * q + 1] = w0 * bf16_hi(x[u][0][q]);
-      }
-#pragma unroll
-      for (int r = 1; r < NMAX; ++r) {
-        if (r < n) {
-          const float wr = p.w[r];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            a[2 * q] = a[2 * q] + wr * bf16_lo(x[u][r][q]);
-            a[2 * q + 1] = a[2 * q + 1] + wr * bf16_hi(x[u][r][q]);
-          }
-        }
-      }
-      f32x4 lo = {a[0], a[1], a[2], a[3]};
-      f32x4 hi = {a[4], a[5], a[6], a[7]};
-      if (ACC) {
-        lo = out[2 * i] + lo;
-        hi = out[2 * i + 1] + hi;
-      }
-      st_nt(lo, out + 2 * i);
-      st_nt(hi, out + 2 * i + 1);
+      f32x4 a = reduce4<NMAX>(x[u], n, p.w);
+      if (ACC) a = out[i] + a;
+      st_nt(a, out + i);
     }
   }
 }
@@ -213,6 +212,82 @@ __global__ __launch_bounds__(kBlock) void adam_scalar_kernel(AdamParams a) {
   }
 }
 
+// ------------------------------------------------ fused reduce-scatter + Adam
+// The reduce-scatter and the owner update in one pass (blog "数据并行与 ZeRO：
+// 三级分片各省多少", section 三级分片: ZeRO-1 places the optimizer step between
+// the reduce-scatter and the all-gather).  The reduced gradient is formed in
+// registers with exactly the reduce-scatter kernel's arithmetic and handed to
+// the same update, so the results are bit-identical to the two kernels run
+// one after the other; it is written out only when gout is given.  Bytes per
+// parameter (N=4): 8 (contributions) + 12 (state) read, 12 (state) + 2 (BF16)
+// written = 34, against 12 + 30 = 42 for the two kernels.
+template <int N, bool WD, bool WG, int U>
+__global__ __launch_bounds__(kBlock) void fused_vec_kernel(FusedParams p) {
+  constexpr int NMAX = N > 0 ? N : ZERO_MAX_RANKS;
+  const int n = N > 0 ? N : p.n_ranks;
+  const int k = blockIdx.y;
+  const int64_t nvec = p.shard >> 2;
+  const int64_t off = static_cast<int64_t>(k) * nvec;
+  f32x4* __restrict__ P = reinterpret_cast<f32x4*>(p.p[k]);
+  f32x4* __restrict__ M = reinterpret_cast<f32x4*>(p.m[k]);
+  f32x4* __restrict__ V = reinterpret_cast<f32x4*>(p.v[k]);
+  u32x2* __restrict__ B = reinterpret_cast<u32x2*>(p.b[k]);
+  f32x4* __restrict__ GO = reinterpret_cast<f32x4*>(p.gout[k]);
+  const int64_t step = static_cast<int64_t>(gridDim.x) * kBlock * U;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock * U + threadIdx.x; base < nvec;
+       base += step) {
+    u32x2 x[U][NMAX];
+    f32x4 pv[U], mv[U], vv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * kBlock;
+      if (i < nvec) {
+#pragma unroll
+        for (int r = 0; r < NMAX; ++r)
+          if (r < n) x[u][r] = ld_nt(reinterpret_cast<const u32x2*>(p.g[r]) + off + i);
+        pv[u] = ld_nt(P + i);
+        mv[u] = ld_nt(M + i);
+        vv[u] = ld_nt(V + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * kBlock;
+      if (i >= nvec) break;
+      const f32x4 g = reduce4<NMAX>(x[u], n, p.w);
+      if (WG) st_nt(g, GO + i);
+      float pe[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
+      float me[4] = {mv[u].x, mv[u].y, mv[u].z, mv[u].w};
+      float ve[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+      const float ge[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) adam_elem<WD>(pe[e], me[e], ve[e], ge[e], p.s);
+      st_nt(f32x4{pe[0], pe[1], pe[2], pe[3]}, P + i);
+      st_nt(f32x4{me[0], me[1], me[2], me[3]}, M + i);
+      st_nt(f32x4{ve[0], ve[1], ve[2], ve[3]}, V + i);
+      st_nt(u32x2{to_bf16x2(pe[0], pe[1]), to_bf16x2(pe[2], pe[3])}, B + i);
+    }
+  }
+}
+
+template <bool WD>
+__global__ __launch_bounds__(kBlock) void fused_scalar_kernel(FusedParams p) {
+  const int k = blockIdx.y;
+  const int64_t base = static_cast<int64_t>(k) * p.shard;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < p.shard;
+       i += static_cast<int64_t>(gridDim.x) * kBlock) {
+    float g = p.w[0] * bf16_at(p.g[0], base + i);
+    for (int r = 1; r < p.n_ranks; ++r) g = g + p.w[r] * bf16_at(p.g[r], base + i);
+    if (p.gout[k]) p.gout[k][i] = g;
+    float pe = p.p[k][i], me = p.m[k][i], ve = p.v[k][i];
+    adam_elem<WD>(pe, me, ve, g, p.s);
+    p.p[k][i] = pe;
+    p.m[k][i] = me;
+    p.v[k][i] = ve;
+    p.b[k][i] = to_bf16(pe);
+  }
+}
+
 // ---------------------------------------------------------------- all-gather
 // The full view is the owners' shards concatenated in owner order (essay,
 // section ZeRO-3 的一次完整计算; slide, note 原 N47).  Owner k = blockIdx.y.
@@ -288,13 +363,14 @@ unsigned grid_x(int64_t units, int u, int n_y) {
 }
 
 // Vectors per lane per loop iteration (measured: 1 is best with full grids).
-constexpr int kRsU = 1;
+constexpr int kRsU = 2;
+constexpr int kFusedU = 1;
 constexpr int kAdamU = 1;
 constexpr int kGatherU = 1;
 
 template <int N, bool ACC>
 hipError_t rs_vec_launch(const RsParams& p, int n_shards, hipStream_t s) {
-  dim3 grid(grid_x(p.shard >> 3, kRsU, n_shards), n_shards);
+  dim3 grid(grid_x(p.shard >> 2, kRsU, n_shards), n_shards);
   hipLaunchKernelGGL((rs_vec_kernel<N, ACC, kRsU>), grid, dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
@@ -321,6 +397,38 @@ hipError_t launch_reduce_scatter(const RsParams& p, int n_shards, bool accumulat
                                  hipStream_t stream) {
   return accumulate ? rs_dispatch<true>(p, n_shards, vec, stream)
                     : rs_dispatch<false>(p, n_shards, vec, stream);
+}
+
+template <int N, bool WD, bool WG>
+hipError_t fused_vec_launch(const FusedParams& p, int n_shards, hipStream_t s) {
+  dim3 grid(grid_x(p.shard >> 2, kFusedU, n_shards), n_shards);
+  hipLaunchKernelGGL((fused_vec_kernel<N, WD, WG, kFusedU>), grid, dim3(kBlock), 0, s, p);
+  return hipGetLastError();
+}
+
+template <bool WD, bool WG>
+hipError_t fused_dispatch_n(const FusedParams& p, int n_shards, hipStream_t s) {
+  switch (p.n_ranks) {
+    case 1: return fused_vec_launch<1, WD, WG>(p, n_shards, s);
+    case 2: return fused_vec_launch<2, WD, WG>(p, n_shards, s);
+    case 4: return fused_vec_launch<4, WD, WG>(p, n_shards, s);
+    case 8: return fused_vec_launch<8, WD, WG>(p, n_shards, s);
+    default: return fused_vec_launch<0, WD, WG>(p, n_shards, s);
+  }
+}
+
+hipError_t launch_fused(const FusedParams& p, int n_shards, bool write_grad, bool vec, hipStream_t s) {
+  const bool wd = p.s.weight_decay != 0.0f;
+  if (!vec) {
+    dim3 grid(grid_x(p.shard, 1, n_shards), n_shards);
+    if (wd)
+      hipLaunchKernelGGL((fused_scalar_kernel<true>), grid, dim3(kBlock), 0, s, p);
+    else
+      hipLaunchKernelGGL((fused_scalar_kernel<false>), grid, dim3(kBlock), 0, s, p);
+    return hipGetLastError();
+  }
+  if (wd) return write_grad ? fused_dispatch_n<true, true>(p, n_shards, s) : fused_dispatch_n<true, false>(p, n_shards, s);
+  return write_grad ? fused_dispatch_n<false, true>(p, n_shards, s) : fused_dispatch_n<false, false>(p, n_shards, s);
 }
 
 hipError_t launch_adam(const AdamParams& a, bool vec, hipStream_t s) {

@@ -207,11 +207,11 @@ int zero_offload_stream(zero_offload* h, int op, int64_t chunk, int micro_batch,
     memset(&p, 0, sizeof p);
     p.shard = len;
     p.n_ranks = h->n_ranks;
-    bool vec = (len % 8) == 0 && aligned16(h->stage[s]);
+    bool vec = (len % 4) == 0 && aligned16(h->stage[s]);
     for (int r = 0; r < h->n_ranks; ++r) {
       p.g[r] = g[r];
       p.w[r] = rank_weights[r];
-      vec = vec && aligned16(g[r]);
+      vec = vec && aligned8(g[r]);
     }
     p.out[0] = h->stage[s];
     set_path(vec);

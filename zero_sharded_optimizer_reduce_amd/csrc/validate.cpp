@@ -71,6 +71,57 @@ int check_reduce_scatter(const uint16_t* const* rank_grads, const float* rank_we
   return ZERO_OK;
 }
 
+int check_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* rank_weights,
+                              int n_ranks, int64_t numel, int n_shards, float* const* master,
+                              float* const* exp_avg, float* const* exp_avg_sq,
+                              uint16_t* const* bf16_out, float* const* grad_out,
+                              const zero_adam_hparams* hp, Err& e) {
+  int st = check_adam_hparams(hp, e);
+  if (st) return st;
+  if (!rank_grads || !rank_weights || !master || !exp_avg || !exp_avg_sq || !bf16_out)
+    return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: NULL pointer table or weights");
+  if (n_ranks < 1 || n_ranks > ZERO_MAX_RANKS)
+    return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: n_ranks=%d outside [1,%d]", n_ranks, ZERO_MAX_RANKS);
+  if (n_shards < 1 || n_shards > ZERO_MAX_RANKS)
+    return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: n_shards=%d outside [1,%d]", n_shards, ZERO_MAX_RANKS);
+  if (numel < 0) return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: numel < 0");
+  if (numel % n_shards != 0)
+    return set_err(e, ZERO_ERR_SIZE, "reduce_scatter_adam: numel=%lld not divisible by n_shards=%d",
+                   (long long)numel, n_shards);
+  if (mul_overflows(numel, 4)) return set_err(e, ZERO_ERR_SIZE, "reduce_scatter_adam: numel too large");
+  if (numel == 0) return ZERO_OK;
+  const int64_t shard = numel / n_shards;
+  Range rs[ZERO_MAX_RANKS * 6];
+  int nr = 0;
+  for (int r = 0; r < n_ranks; ++r) {
+    if (!rank_grads[r]) return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: rank_grads[%d] is NULL", r);
+    if (reinterpret_cast<uintptr_t>(rank_grads[r]) & 1u)
+      return set_err(e, ZERO_ERR_ALIGN, "reduce_scatter_adam: rank_grads[%d] not 2-byte aligned", r);
+  }
+  for (int k = 0; k < n_shards; ++k) {
+    const void* f32s[4] = {master[k], exp_avg[k], exp_avg_sq[k], grad_out ? grad_out[k] : nullptr};
+    for (int j = 0; j < 4; ++j) {
+      if (j < 3 && !f32s[j]) return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: NULL state of owner %d", k);
+      if (j == 3 && grad_out && !f32s[j])
+        return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: grad_out[%d] is NULL", k);
+      if (reinterpret_cast<uintptr_t>(f32s[j]) & 3u)
+        return set_err(e, ZERO_ERR_ALIGN, "reduce_scatter_adam: FP32 buffer of owner %d misaligned", k);
+      if (f32s[j]) rs[nr++] = range_of(f32s[j], shard * 4);
+    }
+    if (!bf16_out[k]) return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: bf16_out[%d] is NULL", k);
+    if (reinterpret_cast<uintptr_t>(bf16_out[k]) & 1u)
+      return set_err(e, ZERO_ERR_ALIGN, "reduce_scatter_adam: bf16_out[%d] misaligned", k);
+    rs[nr++] = range_of(bf16_out[k], shard * 2);
+  }
+  const int n_out = nr;
+  for (int r = 0; r < n_ranks; ++r) rs[nr++] = range_of(rank_grads[r], numel * 2);
+  for (int i = 0; i < n_out; ++i)
+    for (int j = i + 1; j < nr; ++j)
+      if (overlaps(rs[i], rs[j]))
+        return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: an output buffer overlaps another buffer");
+  return ZERO_OK;
+}
+
 int check_adam_hparams(const zero_adam_hparams* hp, Err& e) {
   if (!hp) return set_err(e, ZERO_ERR_ARG, "adam: NULL hyper-parameters");
   if (hp->step < 1) return set_err(e, ZERO_ERR_ARG, "adam: step=%lld < 1", (long long)hp->step);

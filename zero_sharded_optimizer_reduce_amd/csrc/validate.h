@@ -48,7 +48,14 @@ int rank_weights(const int64_t* counts, int n_ranks, float* out, Err& e);
 int shard_layout(const int64_t* numels, int n_tensors, int n_shards, int64_t* psi,
                  int64_t* psi_pad, int64_t* shard_numel, Err& e);
 
-// True when every pointer is 16-byte aligned: the kernels' 128-bit path.
+int check_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* rank_weights,
+                              int n_ranks, int64_t numel, int n_shards, float* const* master,
+                              float* const* exp_avg, float* const* exp_avg_sq,
+                              uint16_t* const* bf16_out, float* const* grad_out,
+                              const zero_adam_hparams* hp, Err& e);
+
+// Alignment tests for the kernels' vector paths.
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 }  // namespace zero

@@ -80,11 +80,11 @@ int zero_reduce_scatter(const uint16_t* const* rank_grads, const float* rank_wei
   memset(&p, 0, sizeof p);
   p.shard = numel / n_shards;
   p.n_ranks = n_ranks;
-  bool vec = (p.shard % 8) == 0;
+  bool vec = (p.shard % 4) == 0;
   for (int r = 0; r < n_ranks; ++r) {
     p.g[r] = rank_grads[r];
     p.w[r] = rank_weights[r];
-    vec = vec && aligned16(rank_grads[r]);
+    vec = vec && aligned8(rank_grads[r]);
   }
   for (int k = 0; k < n_shards; ++k) {
     p.out[k] = shards_out[k];
@@ -114,6 +114,41 @@ int zero_adam_shard_step(float* master, float* exp_avg, float* exp_avg_sq, uint1
                    aligned16(grad) && (reinterpret_cast<uintptr_t>(bf16_out) & 7u) == 0;
   set_path(vec);
   return hip_status(launch_adam(a, vec, static_cast<hipStream_t>(stream)), "zero_adam_shard_step");
+}
+
+int zero_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* rank_weights,
+                             int n_ranks, int64_t numel, int n_shards, float* const* master,
+                             float* const* exp_avg, float* const* exp_avg_sq,
+                             uint16_t* const* bf16_out, float* const* grad_out,
+                             const zero_adam_hparams* hp, void* stream) {
+  Err e;
+  int st = check_reduce_scatter_adam(rank_grads, rank_weights, n_ranks, numel, n_shards, master,
+                                     exp_avg, exp_avg_sq, bf16_out, grad_out, hp, e);
+  if (st) return fail(st, e.msg);
+  if (numel == 0) return ZERO_OK;
+  FusedParams p;
+  memset(&p, 0, sizeof p);
+  p.shard = numel / n_shards;
+  p.n_ranks = n_ranks;
+  adam_scalars(hp, &p.s, e);
+  bool vec = (p.shard % 4) == 0;
+  for (int r = 0; r < n_ranks; ++r) {
+    p.g[r] = rank_grads[r];
+    p.w[r] = rank_weights[r];
+    vec = vec && aligned8(rank_grads[r]);
+  }
+  for (int k = 0; k < n_shards; ++k) {
+    p.p[k] = master[k];
+    p.m[k] = exp_avg[k];
+    p.v[k] = exp_avg_sq[k];
+    p.b[k] = bf16_out[k];
+    p.gout[k] = grad_out ? grad_out[k] : nullptr;
+    vec = vec && aligned16(p.p[k]) && aligned16(p.m[k]) && aligned16(p.v[k]) && aligned8(p.b[k]) &&
+          aligned16(p.gout[k]);
+  }
+  set_path(vec);
+  return hip_status(launch_fused(p, n_shards, grad_out != nullptr, vec, static_cast<hipStream_t>(stream)),
+                    "zero_reduce_scatter_adam");
 }
 
 int zero_all_gather_layer(const void* const* shards, int n_shards, int64_t shard_bytes,
