@@ -47,6 +47,7 @@ extern "C" {
 #endif
 
 #define ZERO_MAX_RANKS 16   /* upper bound on n_ranks and n_shards */
+#define ZERO_NORM_BLOCKS 1024  /* partial sums per shard in zero_grad_norm_sq */
 
 typedef enum zero_status {
   ZERO_OK = 0,
@@ -124,6 +125,15 @@ int zero_reduce_scatter(const uint16_t* const* rank_grads, const float* rank_wei
                         int64_t numel, float* const* shards_out, int n_shards, int accumulate,
                         void* stream);
 
+/* zero_reduce_scatter for FP32 contributions (gradients kept in FP32: the
+ * +2 bytes per parameter variant of [blog] 每个参数 16 字节).  Same
+ * arithmetic and order; rank_grads[r] points to numel FP32 values (4-byte
+ * aligned).  The vector path needs 16-byte aligned pointers and
+ * numel/n_shards % 4 == 0. */
+int zero_reduce_scatter_f32(const float* const* rank_grads, const float* rank_weights, int n_ranks,
+                            int64_t numel, float* const* shards_out, int n_shards, int accumulate,
+                            void* stream);
+
 /* Owner update: one fused pass of mixed-precision Adam/AdamW over n elements
  * of the owner's shard ([slide] note 原 N48: the owner updates its master
  * weights and m/v with the combined gradient; [essay] 从持久状态开始记账 and
@@ -142,6 +152,33 @@ int zero_reduce_scatter(const uint16_t* const* rank_grads, const float* rank_wei
  * ZERO_ERR_ALIGN, ZERO_ERR_HIP. */
 int zero_adam_shard_step(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* bf16_out,
                          const float* grad, int64_t n, const zero_adam_hparams* hp, void* stream);
+
+/* zero_adam_shard_step with the gradient first multiplied by a device scalar:
+ * g = g * (*grad_scale) (one binary32 multiply), then the same update.  Used
+ * with the clip coefficient of zero_grad_norm_sq, which stays on the device.
+ *   grad_scale   device pointer to one float (4-byte aligned), read once.
+ * Errors: as zero_adam_shard_step; ZERO_ERR_ARG for a NULL grad_scale. */
+int zero_adam_shard_step_scaled(float* master, float* exp_avg, float* exp_avg_sq,
+                                uint16_t* bf16_out, const float* grad, const float* grad_scale,
+                                int64_t n, const zero_adam_hparams* hp, void* stream);
+
+/* Global gradient norm and clip coefficient (optional; the pages do not
+ * describe clipping).  norm_sq_out[0] = sum over the shards of x*x, each square
+ * exact in FP64 and the additions in FP64 in an order fixed by shard_numel and
+ * n_shards alone (per shard ZERO_NORM_BLOCKS or fewer lane-sequential partial
+ * sums, a butterfly over each 64-lane wave, the 4 waves of a block in order,
+ * then the per-block partial sums in index order), so repeated calls give the
+ * same bits on any device.  If clip_coef_out is not NULL it receives
+ * float(min(1, max_norm / (sqrt(norm_sq) + 1e-6))) computed in FP64.
+ *   shards       host array of n_shards device pointers to FP32[shard_numel].
+ *   workspace    device scratch of workspace_len >= n_shards*ZERO_NORM_BLOCKS
+ *                doubles (8-byte aligned), overwritten.
+ *   norm_sq_out  device pointer to one double.
+ * Errors: ZERO_ERR_ARG (NULL, counts, overlap, max_norm <= 0 with a clip
+ * output), ZERO_ERR_SIZE (workspace too small), ZERO_ERR_ALIGN, ZERO_ERR_HIP. */
+int zero_grad_norm_sq(const float* const* shards, int n_shards, int64_t shard_numel,
+                      double* workspace, int64_t workspace_len, double* norm_sq_out,
+                      float max_norm, float* clip_coef_out, void* stream);
 
 /* Reduce-scatter and owner update in one pass ([blog] 三级分片, ZeRO-1: the
  * optimizer step sits between the reduce-scatter and the all-gather).  For

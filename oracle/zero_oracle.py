@@ -162,6 +162,13 @@ def _f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # a3: element-wise weighted reduction (all-reduce result) and reduce-scatter
 # ---------------------------------------------------------------------------
+def _contribution_f32(x: np.ndarray) -> np.ndarray:
+    """A rank's contribution as float32: BF16 bit patterns are widened exactly;
+    FP32 contributions (gradients stored in FP32, the blog's +2 bytes variant in
+    section 每个参数 16 字节) are used as they are."""
+    x = np.asarray(x)
+    return bf16_to_f32(x) if x.dtype == U16 else _chk32(x)
+
 def reduce_full(rank_grads: Sequence[np.ndarray], weights: np.ndarray) -> np.ndarray:
     """The combined gradient of every parameter: sum_r w_r * g_r, in FP32.
 
@@ -171,10 +178,11 @@ def reduce_full(rank_grads: Sequence[np.ndarray], weights: np.ndarray) -> np.nda
     """
     weights = np.asarray(weights)
     assert weights.dtype == F32 and len(rank_grads) == weights.size >= 1
-    a = _chk32(weights[0] * bf16_to_f32(rank_grads[0]))
-    for r in range(1, len(rank_grads)):
-        term = _chk32(weights[r] * bf16_to_f32(rank_grads[r]))
-        a = _chk32(a + term)
+    with np.errstate(all="ignore"):       # IEEE propagation of inf/NaN is intended
+        a = _chk32(weights[0] * _contribution_f32(rank_grads[0]))
+        for r in range(1, len(rank_grads)):
+            term = _chk32(weights[r] * _contribution_f32(rank_grads[r]))
+            a = _chk32(a + term)
     return a
 
 
@@ -190,7 +198,7 @@ def reduce_owner_shard(rank_grads: Sequence[np.ndarray], weights: np.ndarray,
     lo, hi = shard_bounds(rank_grads[0].size, n_shards, k)
     a = None
     for r, g in enumerate(rank_grads):
-        term = _chk32(weights[r] * bf16_to_f32(g[lo:hi]))
+        term = _chk32(weights[r] * _contribution_f32(g[lo:hi]))
         a = term if a is None else _chk32(a + term)
     return a
 
@@ -317,6 +325,33 @@ def offload_accumulate(per_micro_batch_grads: Sequence[Sequence[np.ndarray]], we
         r = reduce_full(grads, weights)
         acc = r if acc is None else _chk32(acc + r)
     return acc
+
+
+# ---------------------------------------------------------------------------
+# Optional global gradient norm and clipping (not described by the pages; the
+# plain reading: the Euclidean norm of the whole reduced gradient, and the
+# gradient scaled by min(1, max_norm / (norm + 1e-6)) before the update)
+# ---------------------------------------------------------------------------
+def grad_norm_sq(shards: Sequence[np.ndarray]) -> float:
+    """Sum of squares of every element of every shard, in float64 (the squares
+    of binary32 values are exact in binary64)."""
+    total = 0.0
+    for x in shards:
+        x64 = _chk32(np.asarray(x)).astype(np.float64)
+        total += float(np.sum(x64 * x64))
+    return total
+
+
+def clip_coefficient(norm_sq: float, max_norm: float) -> np.float32:
+    """float32(min(1, max_norm / (sqrt(norm_sq) + 1e-6))), evaluated in float64."""
+    c = float(np.float32(max_norm)) / (math.sqrt(norm_sq) + 1e-6)
+    return np.float32(min(1.0, c))
+
+
+def scale_grad(g: np.ndarray, coef: np.float32) -> np.ndarray:
+    """The clipped gradient: one binary32 multiply per element."""
+    assert type(coef) is np.float32
+    return _chk32(_chk32(np.asarray(g)) * coef)
 
 
 # ---------------------------------------------------------------------------

@@ -188,3 +188,22 @@ def test_all_gather(dtype, shard_elems, n_shards):
     got = view.view(torch.uint8).cpu().numpy()
     ref = oracle.all_gather([s.view(torch.uint8).cpu().numpy() for s in shards])
     assert np.array_equal(got, ref)
+
+
+# --------------------------------------------- FP32 contributions (gradients kept in FP32)
+@pytest.mark.parametrize("n_ranks,per_shard", [(4, 4096 + 4), (3, 1024), (4, 37), (1, 8), (16, 64)])
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_reduce_scatter_f32_contributions(n_ranks, per_shard, accumulate):
+    n_shards = n_ranks
+    numel = per_shard * n_shards
+    rng = np.random.default_rng(8000 + per_shard + n_ranks)
+    grads = [S.normal_f32(rng, numel, 1e-3) for _ in range(n_ranks)]
+    w = oracle.weights_from_counts(list(range(2, 2 + n_ranks)))
+    init = [S.normal_f32(rng, per_shard, 1e-3) for _ in range(n_shards)]
+    out = [f32_to_dev(x) for x in init]
+    z.zero_reduce_scatter_f32([f32_to_dev(g) for g in grads], w, out, accumulate=accumulate)
+    assert z.zero_last_path_vectorized() == (1 if per_shard % 4 == 0 else 0)
+    for k in range(n_shards):
+        red = oracle.reduce_owner_shard(grads, w, n_shards, k)
+        ref = init[k] + red if accumulate else red
+        assert_grad_exact(f32_to_host(out[k]), ref, f"shard {k}")

@@ -177,3 +177,31 @@ def test_special_values_propagate():
     assert p1[4] == 0 and np.signbit(p1[4])   # -0 - lr*0 = -0
     # bf16 of a NaN is a NaN
     assert (int(b[0]) & 0x7FFF) > 0x7F80
+
+
+# ----------------------------------------------------- optional gradient clipping
+def test_grad_norm_sq_is_the_exact_sum_of_squares():
+    from fractions import Fraction
+    rng = np.random.default_rng(21)
+    shards = [S.normal_f32(rng, 300, 1e-3) for _ in range(3)]
+    exact = sum(Fraction(float(x)) ** 2 for s in shards for x in s)
+    got = oracle.grad_norm_sq(shards)
+    assert abs(Fraction(got) - exact) <= exact * Fraction(1, 10 ** 12)
+    assert oracle.grad_norm_sq([np.array([3.0, 4.0], np.float32)]) == 25.0
+    assert oracle.grad_norm_sq([np.full(1000, 0.5, np.float32)]) == 250.0
+    assert oracle.grad_norm_sq([np.zeros(0, np.float32)]) == 0.0
+
+
+def test_clip_coefficient_closed_forms():
+    assert oracle.clip_coefficient(0.25, 1.0) == np.float32(1.0)          # norm 0.5 below the limit
+    assert oracle.clip_coefficient(1.0, 1.0) == np.float32(1.0 / (1.0 + 1e-6))
+    c = oracle.clip_coefficient(4.0, 1.0)                                 # norm 2: halve
+    assert abs(float(c) - 0.5) < 1e-6
+    # after clipping, the norm is max_norm (to within the eps and rounding)
+    rng = np.random.default_rng(22)
+    g = S.normal_f32(rng, 4096, 1.0)
+    c = oracle.clip_coefficient(oracle.grad_norm_sq([g]), 2.0)
+    assert abs(math.sqrt(oracle.grad_norm_sq([oracle.scale_grad(g, c)])) - 2.0) < 1e-5
+    # scaling by 1 or a power of two is exact
+    assert np.array_equal(oracle.scale_grad(g, np.float32(1.0)), g)
+    assert np.array_equal(oracle.scale_grad(g, np.float32(0.25)), g / np.float32(4))

@@ -25,8 +25,8 @@ MUTATIONS = {
     "owner_slice_shifted": ("    lo, hi = shard_bounds(rank_grads[0].size, n_shards, k)\n",
                             "    lo, hi = shard_bounds(rank_grads[0].size, n_shards, k)\n"
                             "    lo, hi = (lo + 1, hi + 1) if hi < rank_grads[0].size else (lo, hi)\n"),
-    "weight_paired_with_wrong_rank": ("term = _chk32(weights[r] * bf16_to_f32(rank_grads[r]))",
-                                      "term = _chk32(weights[(r + 1) % len(rank_grads)] * bf16_to_f32(rank_grads[r]))"),
+    "weight_paired_with_wrong_rank": ("term = _chk32(weights[r] * _contribution_f32(rank_grads[r]))",
+                                      "term = _chk32(weights[(r + 1) % len(rank_grads)] * _contribution_f32(rank_grads[r]))"),
     "bf16_ties_away": ("take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & lo_odd)", "take_hi = (d_hi <= d_lo)"),
     "bf16_truncates": ("take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & lo_odd)", "take_hi = d_hi < 0"),
     "bf16_widen_shift": ("<< U32(16)).view(F32)", "<< U32(15)).view(F32)"),
@@ -35,6 +35,9 @@ MUTATIONS = {
     "padding_rule": ("psi_pad = ((psi + q - 1) // q) * q", "psi_pad = ((psi + q) // q) * q"),
     "gather_order": ("full = np.concatenate(list(shards))", "full = np.concatenate(list(shards)[::-1])"),
     "offload_not_accumulated": ("acc = r if acc is None else _chk32(acc + r)", "acc = r"),
+    "norm_not_squared": ("total += float(np.sum(x64 * x64))", "total += float(np.sum(np.abs(x64)))"),
+    "clip_uses_norm_sq": ("c = float(np.float32(max_norm)) / (math.sqrt(norm_sq) + 1e-6)",
+                          "c = float(np.float32(max_norm)) / (norm_sq + 1e-6)"),
     "accumulate_mode_drops_acc": ("return _chk32(acc + reduce_full(rank_grads, weights))",
                                   "return _chk32(reduce_full(rank_grads, weights))"),
 }

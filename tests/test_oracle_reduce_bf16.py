@@ -115,6 +115,23 @@ def test_weighted_reduce_within_summation_bound_of_exact(n):
                 sum(abs(Fraction(float(w[r])) * Fraction(float(xs[r][i]))) for r in range(n)))
 
 
+@pytest.mark.parametrize("n", [1, 3, 4])
+def test_fp32_contributions_within_summation_bound_of_exact(n):
+    rng = np.random.default_rng(300 + n)
+    psi = 128 * n
+    g = [S.normal_f32(rng, psi, 1e-3, float(rng.uniform(0.5, 2.0))) for _ in range(n)]
+    w = oracle.weights_from_counts(list(rng.integers(1, 5000, n)))
+    a = oracle.reduce_full(g, w)
+    gamma = n * U / (1 - n * U)
+    for i in range(0, psi, 7):
+        terms = [Fraction(float(w[r])) * Fraction(float(g[r][i])) for r in range(n)]
+        assert abs(float(Fraction(float(a[i])) - sum(terms))) <= gamma * float(sum(abs(t) for t in terms))
+    # BF16-valued FP32 contributions reduce exactly like the BF16 bit patterns
+    gb = [S.to_bf16_bits(x) for x in g]
+    assert np.array_equal(oracle.reduce_full([oracle.bf16_to_f32(x) for x in gb], w).view(np.uint32),
+                          oracle.reduce_full(gb, w).view(np.uint32))
+
+
 def test_reduce_exact_when_representable():
     # small integers scaled by 2^-10 with power-of-two weights: every partial
     # sum is representable, so the reduction is the exact value

@@ -10,7 +10,9 @@ from .api import (  # noqa: F401
     ZeroOffload,
     zero_adam_scalars_compute,
     zero_adam_shard_step,
+    zero_adam_shard_step_scaled,
     zero_all_gather_layer,
+    zero_grad_norm_sq,
     zero_last_path_vectorized,
     zero_offload_create,
     zero_offload_destroy,
@@ -19,5 +21,6 @@ from .api import (  # noqa: F401
     zero_rank_weights,
     zero_reduce_scatter,
     zero_reduce_scatter_adam,
+    zero_reduce_scatter_f32,
     zero_shard_layout,
 )

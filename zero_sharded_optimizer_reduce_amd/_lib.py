@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzero.so"
 
 ZERO_OK, ZERO_ERR_ARG, ZERO_ERR_ALIGN, ZERO_ERR_SIZE, ZERO_ERR_HIP, ZERO_ERR_STATE = 0, -1, -2, -3, -4, -5
 ZERO_MAX_RANKS = 16
+ZERO_NORM_BLOCKS = 1024
 ZERO_OFFLOAD_REDUCE, ZERO_OFFLOAD_ADAM = 0, 1
 
 
@@ -38,7 +39,10 @@ SIGNATURES = {
     "zero_rank_weights": (C.c_int, [I64P, C.c_int, FP]),
     "zero_shard_layout": (C.c_int, [I64P, C.c_int, C.c_int, I64P, I64P, I64P]),
     "zero_reduce_scatter": (C.c_int, [PP, FP, C.c_int, I64, PP, C.c_int, C.c_int, P]),
+    "zero_reduce_scatter_f32": (C.c_int, [PP, FP, C.c_int, I64, PP, C.c_int, C.c_int, P]),
     "zero_adam_shard_step": (C.c_int, [P, P, P, P, P, I64, C.POINTER(AdamHparams), P]),
+    "zero_adam_shard_step_scaled": (C.c_int, [P, P, P, P, P, P, I64, C.POINTER(AdamHparams), P]),
+    "zero_grad_norm_sq": (C.c_int, [PP, C.c_int, I64, P, I64, P, C.c_float, P, P]),
     "zero_reduce_scatter_adam": (C.c_int, [PP, FP, C.c_int, I64, C.c_int, PP, PP, PP, PP, PP,
                                            C.POINTER(AdamHparams), P]),
     "zero_all_gather_layer": (C.c_int, [PP, C.c_int, I64, P, P]),

@@ -78,13 +78,23 @@ def zero_shard_layout(numels: Sequence[int], n_shards: int):
 def zero_reduce_scatter(rank_grads: Sequence[torch.Tensor], rank_weights, shards_out: Sequence[torch.Tensor],
                         accumulate: bool = False, stream=None) -> None:
     """Owner k's shard = sum_r w_r * float(rank_grads[r][k*S:(k+1)*S]) (rank order),
-    or shard += that sum when accumulate.  rank_grads: BF16 device tensors of
-    equal numel; shards_out: FP32 device tensors of numel/len(shards_out) each."""
+    or shard += that sum when accumulate.  rank_grads: BF16 (zero_reduce_scatter)
+    or FP32 (zero_reduce_scatter_f32) device tensors of equal numel; shards_out:
+    FP32 device tensors of numel/len(shards_out) each."""
+    _reduce_scatter(rank_grads, rank_weights, shards_out, accumulate, stream, f32=False)
+
+
+def zero_reduce_scatter_f32(rank_grads, rank_weights, shards_out, accumulate: bool = False, stream=None) -> None:
+    _reduce_scatter(rank_grads, rank_weights, shards_out, accumulate, stream, f32=True)
+
+
+def _reduce_scatter(rank_grads, rank_weights, shards_out, accumulate, stream, f32):
+    name = "zero_reduce_scatter_f32" if f32 else "zero_reduce_scatter"
     n_ranks, n_shards = len(rank_grads), len(shards_out)
     if n_ranks < 1 or n_shards < 1:
-        raise ValueError("zero_reduce_scatter: need at least one rank and one shard")
+        raise ValueError(f"{name}: need at least one rank and one shard")
     numel = rank_grads[0].numel()
-    gp = [_dev(g, f"rank_grads[{r}]", _BF16_LIKE) for r, g in enumerate(rank_grads)]
+    gp = [_dev(g, f"rank_grads[{r}]", (torch.float32,) if f32 else _BF16_LIKE) for r, g in enumerate(rank_grads)]
     if any(g.numel() != numel for g in rank_grads):
         raise ValueError("zero_reduce_scatter: rank contributions differ in size")
     if numel % n_shards:
@@ -95,9 +105,8 @@ def zero_reduce_scatter(rank_grads: Sequence[torch.Tensor], rank_weights, shards
     w = np.ascontiguousarray(np.asarray(rank_weights, dtype=np.float32))
     if w.size != n_ranks:
         raise ValueError("zero_reduce_scatter: one weight per rank")
-    check(load().zero_reduce_scatter(_ptrs(gp), w.ctypes.data_as(_lib.FP), n_ranks, numel, _ptrs(op),
-                                     n_shards, int(bool(accumulate)), _stream(stream)),
-          "zero_reduce_scatter")
+    check(getattr(load(), name)(_ptrs(gp), w.ctypes.data_as(_lib.FP), n_ranks, numel, _ptrs(op),
+                                n_shards, int(bool(accumulate)), _stream(stream)), name)
 
 
 def zero_adam_shard_step(master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor,
@@ -111,6 +120,46 @@ def zero_adam_shard_step(master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq
         raise ValueError("zero_adam_shard_step: all buffers must have the same numel")
     h = hparams(hp)
     check(load().zero_adam_shard_step(*ptrs, n, C.byref(h), _stream(stream)), "zero_adam_shard_step")
+
+
+def zero_adam_shard_step_scaled(master, exp_avg, exp_avg_sq, bf16_out, grad, grad_scale: torch.Tensor, hp,
+                                stream=None) -> None:
+    """zero_adam_shard_step on grad * grad_scale[0] (a one-element FP32 device
+    tensor, e.g. the clip coefficient from zero_grad_norm_sq)."""
+    n = master.numel()
+    ptrs = [_dev(master, "master", (torch.float32,)), _dev(exp_avg, "exp_avg", (torch.float32,)),
+            _dev(exp_avg_sq, "exp_avg_sq", (torch.float32,)), _dev(bf16_out, "bf16_out", _BF16_LIKE),
+            _dev(grad, "grad", (torch.float32,)), _dev(grad_scale, "grad_scale", (torch.float32,))]
+    if any(t.numel() != n for t in (exp_avg, exp_avg_sq, bf16_out, grad)) or grad_scale.numel() < 1:
+        raise ValueError("zero_adam_shard_step_scaled: size mismatch")
+    h = hparams(hp)
+    check(load().zero_adam_shard_step_scaled(*ptrs, n, C.byref(h), _stream(stream)),
+          "zero_adam_shard_step_scaled")
+
+
+def zero_grad_norm_sq(shards: Sequence[torch.Tensor], workspace: torch.Tensor, norm_sq_out: torch.Tensor,
+                      max_norm: float = 0.0, clip_coef_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """norm_sq_out[0] (FP64 device tensor) = sum of squares of all shards
+    (deterministic order); clip_coef_out[0] (FP32) = min(1, max_norm/(norm+1e-6))
+    when given.  workspace: FP64 device tensor of >= len(shards)*1024 elements."""
+    n = len(shards)
+    if n < 1:
+        raise ValueError("zero_grad_norm_sq: no shards")
+    numel = shards[0].numel()
+    sp = [_dev(t, f"shards[{k}]", (torch.float32,)) for k, t in enumerate(shards)]
+    if any(t.numel() != numel for t in shards):
+        raise ValueError("zero_grad_norm_sq: shards differ in size")
+    wp = _dev(workspace, "workspace", (torch.float64,))
+    op = _dev(norm_sq_out, "norm_sq_out", (torch.float64,))
+    if norm_sq_out.numel() < 1:
+        raise ValueError("zero_grad_norm_sq: norm_sq_out needs one element")
+    cp = None
+    if clip_coef_out is not None:
+        cp = _dev(clip_coef_out, "clip_coef_out", (torch.float32,))
+        if clip_coef_out.numel() < 1:
+            raise ValueError("zero_grad_norm_sq: clip_coef_out needs one element")
+    check(load().zero_grad_norm_sq(_ptrs(sp), n, numel, wp, workspace.numel(), op, float(max_norm), cp,
+                                   _stream(stream)), "zero_grad_norm_sq")
 
 
 def zero_reduce_scatter_adam(rank_grads: Sequence[torch.Tensor], rank_weights, master, exp_avg, exp_avg_sq,

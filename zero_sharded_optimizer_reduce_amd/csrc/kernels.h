@@ -24,8 +24,24 @@ struct AdamParams {
   float* v;
   uint16_t* b;
   const float* g;
+  const float* gscale;  // device scalar multiplying g (gradient clipping), or NULL
   int64_t n;
   zero_adam_scalars s;
+};
+
+// Fixed number of partial sums per shard for the gradient norm, so that the
+// summation order never depends on the device.
+constexpr int kNormBlocks = ZERO_NORM_BLOCKS;
+
+struct NormParams {
+  const float* x[ZERO_MAX_RANKS];  // shards
+  int64_t n;                       // elements per shard
+  double* partials;                // n_shards * gx doubles
+  double* out;                     // sum of squares
+  float* coef;                     // clip coefficient, or NULL
+  float max_norm;
+  int gx;                          // partial sums per shard
+  int n_shards;
 };
 
 struct FusedParams {
@@ -55,10 +71,16 @@ struct GatherParams {
 // output 8-byte aligned.
 hipError_t launch_reduce_scatter(const RsParams& p, int n_shards, bool accumulate, bool vec,
                                  hipStream_t stream);
+// Same with FP32 contributions: p.g holds float pointers (cast).
+hipError_t launch_reduce_scatter_f32(const RsParams& p, int n_shards, bool accumulate, bool vec,
+                                     hipStream_t stream);
 hipError_t launch_adam(const AdamParams& p, bool vec, hipStream_t stream);
 hipError_t launch_fused(const FusedParams& p, int n_shards, bool write_grad, bool vec,
                         hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, int n_shards, int path, hipStream_t stream);
+// Two passes: per-(block, shard) partial sums of squares, then one block
+// folds them in index order and derives the clip coefficient.
+hipError_t launch_norm(NormParams& p, bool vec, hipStream_t stream);
 
 // Fill n 32-bit words with `value` (used to poison released staging buffers
 // in the offload engine's debug mode).

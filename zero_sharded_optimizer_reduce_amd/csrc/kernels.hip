@@ -81,6 +81,50 @@ __device__ __forceinline__ f32x4 reduce4(const u32x2 (&x)[NMAX], int n, const fl
   return f32x4{a0, a1, a2, a3};
 }
 
+template <int NMAX>
+__device__ __forceinline__ f32x4 reduce4(const f32x4 (&x)[NMAX], int n, const float* w) {
+  f32x4 a = w[0] * x[0];
+#pragma unroll
+  for (int r = 1; r < NMAX; ++r)
+    if (r < n) a = a + w[r] * x[r];
+  return a;
+}
+
+// FP32 contributions (gradients stored in FP32): 16-byte load per rank.
+template <int N, bool ACC>
+__global__ __launch_bounds__(kBlock) void rs_f32_vec_kernel(RsParams p) {
+  constexpr int NMAX = N > 0 ? N : ZERO_MAX_RANKS;
+  const int n = N > 0 ? N : p.n_ranks;
+  const int k = blockIdx.y;
+  const int64_t nvec = p.shard >> 2;
+  const int64_t off = static_cast<int64_t>(k) * nvec;
+  f32x4* __restrict__ out = reinterpret_cast<f32x4*>(p.out[k]);
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nvec;
+       i += static_cast<int64_t>(gridDim.x) * kBlock) {
+    f32x4 x[NMAX];
+#pragma unroll
+    for (int r = 0; r < NMAX; ++r)
+      if (r < n) x[r] = ld_nt(reinterpret_cast<const f32x4*>(p.g[r]) + off + i);
+    f32x4 a = reduce4<NMAX>(x, n, p.w);
+    if (ACC) a = out[i] + a;
+    st_nt(a, out + i);
+  }
+}
+
+template <bool ACC>
+__global__ __launch_bounds__(kBlock) void rs_f32_scalar_kernel(RsParams p) {
+  const int k = blockIdx.y;
+  const int64_t base = static_cast<int64_t>(k) * p.shard;
+  float* __restrict__ out = p.out[k];
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < p.shard;
+       i += static_cast<int64_t>(gridDim.x) * kBlock) {
+    const float* const* g = reinterpret_cast<const float* const*>(p.g);
+    float a = p.w[0] * g[0][base + i];
+    for (int r = 1; r < p.n_ranks; ++r) a = a + p.w[r] * g[r][base + i];
+    out[i] = ACC ? out[i] + a : a;
+  }
+}
+
 template <int N, bool ACC, int U>
 __global__ __launch_bounds__(kBlock) void rs_vec_kernel(RsParams p) {
   constexpr int NMAX = N > 0 ? N : ZERO_MAX_RANKS;
@@ -148,8 +192,9 @@ __device__ __forceinline__ void adam_elem(float& p, float& m, float& v, float g,
 
 // One pass: read g, p, m, v (16 B/param), write p, m, v and the BF16 working
 // weight (14 B/param).  Vector path: 4 elements per 16-byte access, U vectors
-// per lane per iteration; the n % 4 tail goes element-wise.
-template <bool WD, int U>
+// per lane per iteration; the n % 4 tail goes element-wise.  SC: the gradient
+// is first multiplied by the device scalar *gscale (the clip coefficient).
+template <bool WD, bool SC, int U>
 __global__ __launch_bounds__(kBlock) void adam_vec_kernel(AdamParams a) {
   const int64_t nvec = a.n >> 2;
   f32x4* __restrict__ P = reinterpret_cast<f32x4*>(a.p);
@@ -157,6 +202,7 @@ __global__ __launch_bounds__(kBlock) void adam_vec_kernel(AdamParams a) {
   f32x4* __restrict__ V = reinterpret_cast<f32x4*>(a.v);
   const f32x4* __restrict__ G = reinterpret_cast<const f32x4*>(a.g);
   u32x2* __restrict__ B = reinterpret_cast<u32x2*>(a.b);
+  const float c = SC ? *a.gscale : 1.0f;
   const int64_t step = static_cast<int64_t>(gridDim.x) * kBlock * U;
   for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock * U + threadIdx.x; base < nvec;
        base += step) {
@@ -175,6 +221,7 @@ __global__ __launch_bounds__(kBlock) void adam_vec_kernel(AdamParams a) {
     for (int u = 0; u < U; ++u) {
       const int64_t i = base + u * kBlock;
       if (i >= nvec) break;
+      if (SC) g[u] = g[u] * c;
       float pe[4] = {p[u].x, p[u].y, p[u].z, p[u].w};
       float me[4] = {m[u].x, m[u].y, m[u].z, m[u].w};
       float ve[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
@@ -191,7 +238,7 @@ __global__ __launch_bounds__(kBlock) void adam_vec_kernel(AdamParams a) {
   if (blockIdx.x == 0 && threadIdx.x < tail) {
     const int64_t i = (nvec << 2) + threadIdx.x;
     float pe = a.p[i], me = a.m[i], ve = a.v[i];
-    adam_elem<WD>(pe, me, ve, a.g[i], a.s);
+    adam_elem<WD>(pe, me, ve, SC ? a.g[i] * c : a.g[i], a.s);
     a.p[i] = pe;
     a.m[i] = me;
     a.v[i] = ve;
@@ -199,16 +246,91 @@ __global__ __launch_bounds__(kBlock) void adam_vec_kernel(AdamParams a) {
   }
 }
 
-template <bool WD>
+template <bool WD, bool SC>
 __global__ __launch_bounds__(kBlock) void adam_scalar_kernel(AdamParams a) {
+  const float c = SC ? *a.gscale : 1.0f;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < a.n;
        i += static_cast<int64_t>(gridDim.x) * kBlock) {
     float pe = a.p[i], me = a.m[i], ve = a.v[i];
-    adam_elem<WD>(pe, me, ve, a.g[i], a.s);
+    adam_elem<WD>(pe, me, ve, SC ? a.g[i] * c : a.g[i], a.s);
     a.p[i] = pe;
     a.m[i] = me;
     a.v[i] = ve;
     a.b[i] = to_bf16(pe);
+  }
+}
+
+// ------------------------------------------------------ global gradient norm
+// Sum of squares of the reduced gradient shards in FP64 (each square of a
+// binary32 value is exact in binary64, so only the additions round), with a
+// summation order fixed by the element count alone: lane-sequential partial
+// sums over a grid-stride pattern of a fixed number of blocks, a butterfly
+// across the 64 lanes of a wave, the 4 waves of a block in order, then one
+// block folding the per-block partial sums in index order.  Repeated calls
+// give the same bits on any device.
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__device__ __forceinline__ double block_sum(double x) {
+  __shared__ double part[kBlock / 64];
+  x = wave_sum(x);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) part[w] = x;
+  __syncthreads();
+  double t = 0.0;
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int i = 0; i < kBlock / 64; ++i) t += part[i];
+  }
+  return t;  // valid in thread 0
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kBlock) void norm_partial_kernel(NormParams p) {
+  const int k = blockIdx.y;
+  const float* __restrict__ x = p.x[k];
+  double acc = 0.0;
+  if (VEC) {
+    const int64_t nvec = p.n >> 2;
+    const f32x4* __restrict__ X = reinterpret_cast<const f32x4*>(x);
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nvec;
+         i += static_cast<int64_t>(gridDim.x) * kBlock) {
+      const f32x4 v = ld_nt(X + i);
+      acc += static_cast<double>(v.x) * static_cast<double>(v.x);
+      acc += static_cast<double>(v.y) * static_cast<double>(v.y);
+      acc += static_cast<double>(v.z) * static_cast<double>(v.z);
+      acc += static_cast<double>(v.w) * static_cast<double>(v.w);
+    }
+    const int64_t tail = p.n - (nvec << 2);
+    if (blockIdx.x == 0 && threadIdx.x < tail) {
+      const double e = x[(nvec << 2) + threadIdx.x];
+      acc += e * e;
+    }
+  } else {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < p.n;
+         i += static_cast<int64_t>(gridDim.x) * kBlock) {
+      const double e = x[i];
+      acc += e * e;
+    }
+  }
+  const double t = block_sum(acc);
+  if (threadIdx.x == 0) p.partials[static_cast<int64_t>(k) * gridDim.x + blockIdx.x] = t;
+}
+
+__global__ __launch_bounds__(kBlock) void norm_final_kernel(NormParams p) {
+  const int64_t total = static_cast<int64_t>(p.n_shards) * p.gx;
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < total; i += kBlock) acc += p.partials[i];
+  const double t = block_sum(acc);
+  if (threadIdx.x == 0) {
+    p.out[0] = t;
+    if (p.coef) {
+      const double c = static_cast<double>(p.max_norm) / (sqrt(t) + 1e-6);
+      p.coef[0] = static_cast<float>(c < 1.0 ? c : 1.0);
+    }
   }
 }
 
@@ -399,6 +521,32 @@ hipError_t launch_reduce_scatter(const RsParams& p, int n_shards, bool accumulat
                     : rs_dispatch<false>(p, n_shards, vec, stream);
 }
 
+template <int N, bool ACC>
+hipError_t rs_f32_vec_launch(const RsParams& p, int n_shards, hipStream_t s) {
+  dim3 grid(grid_x(p.shard >> 2, 1, n_shards), n_shards);
+  hipLaunchKernelGGL((rs_f32_vec_kernel<N, ACC>), grid, dim3(kBlock), 0, s, p);
+  return hipGetLastError();
+}
+
+template <bool ACC>
+hipError_t rs_f32_dispatch(const RsParams& p, int n_shards, bool vec, hipStream_t s) {
+  if (!vec) {
+    dim3 grid(grid_x(p.shard, 1, n_shards), n_shards);
+    hipLaunchKernelGGL((rs_f32_scalar_kernel<ACC>), grid, dim3(kBlock), 0, s, p);
+    return hipGetLastError();
+  }
+  switch (p.n_ranks) {
+    case 4: return rs_f32_vec_launch<4, ACC>(p, n_shards, s);
+    default: return rs_f32_vec_launch<0, ACC>(p, n_shards, s);
+  }
+}
+
+hipError_t launch_reduce_scatter_f32(const RsParams& p, int n_shards, bool accumulate, bool vec,
+                                     hipStream_t stream) {
+  return accumulate ? rs_f32_dispatch<true>(p, n_shards, vec, stream)
+                    : rs_f32_dispatch<false>(p, n_shards, vec, stream);
+}
+
 template <int N, bool WD, bool WG>
 hipError_t fused_vec_launch(const FusedParams& p, int n_shards, hipStream_t s) {
   dim3 grid(grid_x(p.shard >> 2, kFusedU, n_shards), n_shards);
@@ -431,21 +579,39 @@ hipError_t launch_fused(const FusedParams& p, int n_shards, bool write_grad, boo
   return write_grad ? fused_dispatch_n<false, true>(p, n_shards, s) : fused_dispatch_n<false, false>(p, n_shards, s);
 }
 
-hipError_t launch_adam(const AdamParams& a, bool vec, hipStream_t s) {
-  const bool wd = a.s.weight_decay != 0.0f;
+template <bool WD, bool SC>
+hipError_t adam_launch(const AdamParams& a, bool vec, hipStream_t s) {
   if (vec) {
     dim3 grid(grid_x(a.n >> 2, kAdamU, 1));
-    if (wd)
-      hipLaunchKernelGGL((adam_vec_kernel<true, kAdamU>), grid, dim3(kBlock), 0, s, a);
-    else
-      hipLaunchKernelGGL((adam_vec_kernel<false, kAdamU>), grid, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((adam_vec_kernel<WD, SC, kAdamU>), grid, dim3(kBlock), 0, s, a);
   } else {
     dim3 grid(grid_x(a.n, 1, 1));
-    if (wd)
-      hipLaunchKernelGGL((adam_scalar_kernel<true>), grid, dim3(kBlock), 0, s, a);
-    else
-      hipLaunchKernelGGL((adam_scalar_kernel<false>), grid, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((adam_scalar_kernel<WD, SC>), grid, dim3(kBlock), 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_adam(const AdamParams& a, bool vec, hipStream_t s) {
+  const bool wd = a.s.weight_decay != 0.0f;
+  const bool sc = a.gscale != nullptr;
+  if (wd) return sc ? adam_launch<true, true>(a, vec, s) : adam_launch<true, false>(a, vec, s);
+  return sc ? adam_launch<false, true>(a, vec, s) : adam_launch<false, false>(a, vec, s);
+}
+
+hipError_t launch_norm(NormParams& p, bool vec, hipStream_t s) {
+  const int64_t units = vec ? (p.n >> 2) : p.n;
+  int64_t gx = (units + kBlock - 1) / kBlock;
+  if (gx > kNormBlocks) gx = kNormBlocks;
+  if (gx < 1) gx = 1;
+  p.gx = static_cast<int>(gx);
+  dim3 grid(p.gx, p.n_shards);
+  if (vec)
+    hipLaunchKernelGGL((norm_partial_kernel<true>), grid, dim3(kBlock), 0, s, p);
+  else
+    hipLaunchKernelGGL((norm_partial_kernel<false>), grid, dim3(kBlock), 0, s, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(norm_final_kernel, dim3(1), dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 

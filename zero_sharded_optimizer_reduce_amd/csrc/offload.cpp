@@ -194,7 +194,8 @@ int zero_offload_stream(zero_offload* h, int op, int64_t chunk, int micro_batch,
     for (int r = 0; r < h->n_ranks; ++r) g[r] = h->contrib[s] + r * h->chunk;
     float* outp[1] = {h->stage[s]};
     Err e;
-    st = check_reduce_scatter(g, rank_weights, h->n_ranks, len, outp, 1, micro_batch > 0, e);
+    st = check_reduce_scatter(reinterpret_cast<const void* const*>(g), rank_weights, h->n_ranks, len, outp,
+                              1, micro_batch > 0, e);
     if (st) return fail(st, e.msg);
     // staging[s] must be free of its previous D2H reader before it is written
     if (micro_batch > 0) {
@@ -240,6 +241,7 @@ int zero_offload_stream(zero_offload* h, int op, int64_t chunk, int micro_batch,
   st = stream_in(h, chunk, s, len, cs);
   if (st) return st;
   AdamParams a;
+  memset(&a, 0, sizeof a);
   a.p = master + off;
   a.m = exp_avg + off;
   a.v = exp_avg_sq + off;
@@ -248,7 +250,7 @@ int zero_offload_stream(zero_offload* h, int op, int64_t chunk, int micro_batch,
   a.n = len;
   adam_scalars(hp, &a.s, e);
   const bool vec = aligned16(a.p) && aligned16(a.m) && aligned16(a.v) && aligned16(a.g) &&
-                   (reinterpret_cast<uintptr_t>(a.b) & 7u) == 0;
+                   aligned8(a.b);
   set_path(vec);
   ZCHK(launch_adam(a, vec, cs));
   ZCHK(record(h->kernel_done[s], cs));

@@ -29,9 +29,9 @@ static bool mul_overflows(int64_t a, int64_t b) {
   return a != 0 && b > INT64_MAX / a;
 }
 
-int check_reduce_scatter(const uint16_t* const* rank_grads, const float* rank_weights,
+int check_reduce_scatter(const void* const* rank_grads, const float* rank_weights,
                          int n_ranks, int64_t numel, float* const* shards_out, int n_shards,
-                         int accumulate, Err& e) {
+                         int accumulate, Err& e, int elem_bytes) {
   if (!rank_grads || !rank_weights || !shards_out)
     return set_err(e, ZERO_ERR_ARG, "reduce_scatter: NULL pointer table or weights");
   if (n_ranks < 1 || n_ranks > ZERO_MAX_RANKS)
@@ -51,8 +51,8 @@ int check_reduce_scatter(const uint16_t* const* rank_grads, const float* rank_we
   if (numel == 0) return ZERO_OK;
   for (int r = 0; r < n_ranks; ++r) {
     if (!rank_grads[r]) return set_err(e, ZERO_ERR_ARG, "reduce_scatter: rank_grads[%d] is NULL", r);
-    if (reinterpret_cast<uintptr_t>(rank_grads[r]) & 1u)
-      return set_err(e, ZERO_ERR_ALIGN, "reduce_scatter: rank_grads[%d] not 2-byte aligned", r);
+    if (reinterpret_cast<uintptr_t>(rank_grads[r]) & static_cast<uintptr_t>(elem_bytes - 1))
+      return set_err(e, ZERO_ERR_ALIGN, "reduce_scatter: rank_grads[%d] not %d-byte aligned", r, elem_bytes);
   }
   for (int k = 0; k < n_shards; ++k) {
     if (!shards_out[k]) return set_err(e, ZERO_ERR_ARG, "reduce_scatter: shards_out[%d] is NULL", k);
@@ -65,7 +65,7 @@ int check_reduce_scatter(const uint16_t* const* rank_grads, const float* rank_we
       if (overlaps(ok, range_of(shards_out[j], shard * 4)))
         return set_err(e, ZERO_ERR_ARG, "reduce_scatter: shards_out[%d] and [%d] overlap", k, j);
     for (int r = 0; r < n_ranks; ++r)
-      if (overlaps(ok, range_of(rank_grads[r], numel * 2)))
+      if (overlaps(ok, range_of(rank_grads[r], numel * elem_bytes)))
         return set_err(e, ZERO_ERR_ARG, "reduce_scatter: shards_out[%d] overlaps rank_grads[%d]", k, r);
   }
   return ZERO_OK;
@@ -119,6 +119,39 @@ int check_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* ra
     for (int j = i + 1; j < nr; ++j)
       if (overlaps(rs[i], rs[j]))
         return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: an output buffer overlaps another buffer");
+  return ZERO_OK;
+}
+
+int check_grad_norm(const float* const* shards, int n_shards, int64_t shard_numel,
+                    const double* workspace, int64_t workspace_len, const double* norm_sq_out,
+                    float max_norm, const float* clip_coef_out, Err& e) {
+  if (!shards || !workspace || !norm_sq_out)
+    return set_err(e, ZERO_ERR_ARG, "grad_norm: NULL shard table, workspace or output");
+  if (n_shards < 1 || n_shards > ZERO_MAX_RANKS)
+    return set_err(e, ZERO_ERR_ARG, "grad_norm: n_shards=%d outside [1,%d]", n_shards, ZERO_MAX_RANKS);
+  if (shard_numel < 0) return set_err(e, ZERO_ERR_ARG, "grad_norm: shard_numel < 0");
+  if (mul_overflows(shard_numel, 4)) return set_err(e, ZERO_ERR_SIZE, "grad_norm: shard_numel too large");
+  if (workspace_len < static_cast<int64_t>(n_shards) * ZERO_NORM_BLOCKS)
+    return set_err(e, ZERO_ERR_SIZE, "grad_norm: workspace needs n_shards*%d doubles", ZERO_NORM_BLOCKS);
+  if (clip_coef_out && !(max_norm > 0.0f))
+    return set_err(e, ZERO_ERR_ARG, "grad_norm: max_norm must be > 0 when a clip coefficient is requested");
+  const uintptr_t a8 = reinterpret_cast<uintptr_t>(workspace) | reinterpret_cast<uintptr_t>(norm_sq_out);
+  if (a8 & 7u) return set_err(e, ZERO_ERR_ALIGN, "grad_norm: workspace or output not 8-byte aligned");
+  if (clip_coef_out && (reinterpret_cast<uintptr_t>(clip_coef_out) & 3u))
+    return set_err(e, ZERO_ERR_ALIGN, "grad_norm: clip_coef_out not 4-byte aligned");
+  Range outs[3] = {range_of(workspace, workspace_len * 8), range_of(norm_sq_out, 8),
+                   range_of(clip_coef_out, clip_coef_out ? 4 : 0)};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outs[j])) return set_err(e, ZERO_ERR_ARG, "grad_norm: outputs overlap");
+  for (int k = 0; k < n_shards; ++k) {
+    if (shard_numel > 0 && !shards[k]) return set_err(e, ZERO_ERR_ARG, "grad_norm: shards[%d] is NULL", k);
+    if (reinterpret_cast<uintptr_t>(shards[k]) & 3u)
+      return set_err(e, ZERO_ERR_ALIGN, "grad_norm: shards[%d] not 4-byte aligned", k);
+    for (int i = 0; i < 3; ++i)
+      if (overlaps(outs[i], range_of(shards[k], shard_numel * 4)))
+        return set_err(e, ZERO_ERR_ARG, "grad_norm: an output overlaps shards[%d]", k);
+  }
   return ZERO_OK;
 }
 

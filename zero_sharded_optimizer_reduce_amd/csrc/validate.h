@@ -23,9 +23,10 @@ struct Range {
 };
 bool overlaps(Range a, Range b);
 
-int check_reduce_scatter(const uint16_t* const* rank_grads, const float* rank_weights,
+// elem_bytes: 2 for BF16 contributions, 4 for FP32 contributions.
+int check_reduce_scatter(const void* const* rank_grads, const float* rank_weights,
                          int n_ranks, int64_t numel, float* const* shards_out, int n_shards,
-                         int accumulate, Err& e);
+                         int accumulate, Err& e, int elem_bytes = 2);
 
 int check_adam_hparams(const zero_adam_hparams* hp, Err& e);
 
@@ -53,6 +54,10 @@ int check_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* ra
                               float* const* exp_avg, float* const* exp_avg_sq,
                               uint16_t* const* bf16_out, float* const* grad_out,
                               const zero_adam_hparams* hp, Err& e);
+
+int check_grad_norm(const float* const* shards, int n_shards, int64_t shard_numel,
+                    const double* workspace, int64_t workspace_len, const double* norm_sq_out,
+                    float max_norm, const float* clip_coef_out, Err& e);
 
 // Alignment tests for the kernels' vector paths.
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

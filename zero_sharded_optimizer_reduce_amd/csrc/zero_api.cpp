@@ -72,8 +72,8 @@ int zero_reduce_scatter(const uint16_t* const* rank_grads, const float* rank_wei
                         int64_t numel, float* const* shards_out, int n_shards, int accumulate,
                         void* stream) {
   Err e;
-  int st = check_reduce_scatter(rank_grads, rank_weights, n_ranks, numel, shards_out, n_shards,
-                                accumulate, e);
+  int st = check_reduce_scatter(reinterpret_cast<const void* const*>(rank_grads), rank_weights,
+                                n_ranks, numel, shards_out, n_shards, accumulate, e);
   if (st) return fail(st, e.msg);
   if (numel == 0) return ZERO_OK;
   RsParams p;
@@ -96,24 +96,95 @@ int zero_reduce_scatter(const uint16_t* const* rank_grads, const float* rank_wei
                     "zero_reduce_scatter");
 }
 
-int zero_adam_shard_step(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* bf16_out,
-                         const float* grad, int64_t n, const zero_adam_hparams* hp, void* stream) {
+static int adam_common(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* bf16_out,
+                       const float* grad, const float* grad_scale, int64_t n,
+                       const zero_adam_hparams* hp, void* stream, const char* where) {
   Err e;
   int st = check_adam(master, exp_avg, exp_avg_sq, bf16_out, grad, n, hp, e);
   if (st) return fail(st, e.msg);
   if (n == 0) return ZERO_OK;
+  if (grad_scale && (reinterpret_cast<uintptr_t>(grad_scale) & 3u))
+    return fail(ZERO_ERR_ALIGN, "adam: grad_scale not 4-byte aligned");
   AdamParams a;
+  memset(&a, 0, sizeof a);
   a.p = master;
   a.m = exp_avg;
   a.v = exp_avg_sq;
   a.b = bf16_out;
   a.g = grad;
+  a.gscale = grad_scale;
   a.n = n;
   adam_scalars(hp, &a.s, e);
   const bool vec = aligned16(master) && aligned16(exp_avg) && aligned16(exp_avg_sq) &&
-                   aligned16(grad) && (reinterpret_cast<uintptr_t>(bf16_out) & 7u) == 0;
+                   aligned16(grad) && aligned8(bf16_out);
   set_path(vec);
-  return hip_status(launch_adam(a, vec, static_cast<hipStream_t>(stream)), "zero_adam_shard_step");
+  return hip_status(launch_adam(a, vec, static_cast<hipStream_t>(stream)), where);
+}
+
+int zero_reduce_scatter_f32(const float* const* rank_grads, const float* rank_weights, int n_ranks,
+                            int64_t numel, float* const* shards_out, int n_shards, int accumulate,
+                            void* stream) {
+  Err e;
+  int st = check_reduce_scatter(reinterpret_cast<const void* const*>(rank_grads), rank_weights, n_ranks,
+                                numel, shards_out, n_shards, accumulate, e, 4);
+  if (st) return fail(st, e.msg);
+  if (numel == 0) return ZERO_OK;
+  RsParams p;
+  memset(&p, 0, sizeof p);
+  p.shard = numel / n_shards;
+  p.n_ranks = n_ranks;
+  bool vec = (p.shard % 4) == 0;
+  for (int r = 0; r < n_ranks; ++r) {
+    p.g[r] = reinterpret_cast<const uint16_t*>(rank_grads[r]);
+    p.w[r] = rank_weights[r];
+    vec = vec && aligned16(rank_grads[r]);
+  }
+  for (int k = 0; k < n_shards; ++k) {
+    p.out[k] = shards_out[k];
+    vec = vec && aligned16(shards_out[k]);
+  }
+  set_path(vec);
+  return hip_status(launch_reduce_scatter_f32(p, n_shards, accumulate != 0, vec,
+                                              static_cast<hipStream_t>(stream)),
+                    "zero_reduce_scatter_f32");
+}
+
+int zero_adam_shard_step(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* bf16_out,
+                         const float* grad, int64_t n, const zero_adam_hparams* hp, void* stream) {
+  return adam_common(master, exp_avg, exp_avg_sq, bf16_out, grad, nullptr, n, hp, stream,
+                     "zero_adam_shard_step");
+}
+
+int zero_adam_shard_step_scaled(float* master, float* exp_avg, float* exp_avg_sq,
+                                uint16_t* bf16_out, const float* grad, const float* grad_scale,
+                                int64_t n, const zero_adam_hparams* hp, void* stream) {
+  if (!grad_scale && n > 0) return fail(ZERO_ERR_ARG, "adam_scaled: NULL grad_scale");
+  return adam_common(master, exp_avg, exp_avg_sq, bf16_out, grad, grad_scale, n, hp, stream,
+                     "zero_adam_shard_step_scaled");
+}
+
+int zero_grad_norm_sq(const float* const* shards, int n_shards, int64_t shard_numel,
+                      double* workspace, int64_t workspace_len, double* norm_sq_out,
+                      float max_norm, float* clip_coef_out, void* stream) {
+  Err e;
+  int st = check_grad_norm(shards, n_shards, shard_numel, workspace, workspace_len, norm_sq_out,
+                           max_norm, clip_coef_out, e);
+  if (st) return fail(st, e.msg);
+  NormParams p;
+  memset(&p, 0, sizeof p);
+  p.n = shard_numel;
+  p.n_shards = n_shards;
+  p.partials = workspace;
+  p.out = norm_sq_out;
+  p.coef = clip_coef_out;
+  p.max_norm = max_norm;
+  bool vec = true;
+  for (int k = 0; k < n_shards; ++k) {
+    p.x[k] = shards[k];
+    vec = vec && aligned16(shards[k]);
+  }
+  set_path(vec);
+  return hip_status(launch_norm(p, vec, static_cast<hipStream_t>(stream)), "zero_grad_norm_sq");
 }
 
 int zero_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* rank_weights,
