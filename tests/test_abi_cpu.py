@@ -131,3 +131,20 @@ def test_offload_validation(libzero):
     assert L.zero_offload_stream(None, 0, 0, 0, None, None, None, None, None, None, None) == -1
     assert L.zero_offload_sync(None) == -1
     assert L.zero_offload_destroy(None) == 0
+
+
+def test_fused_validation_alias_rules(libzero):
+    from zero_sharded_optimizer_reduce_amd._lib import AdamHparams
+    L = libzero
+    hp = AdamHparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 1)
+    g = _pp(0x10000000)                       # one rank, numel 1024 BF16
+    P, M, V, B = _pp(0x100000), _pp(0x200000), _pp(0x300000), _pp(0x400000)
+    acc = _pp(0x500000)
+    # (grad_out identical to grad_acc is allowed; the GPU tests run that case)
+    # grad_out overlapping grad_acc partially: rejected before any launch
+    assert L.zero_reduce_scatter_adam(g, _w(1), 1, 1024, 1, P, M, V, B, acc, _pp(0x500010), C.byref(hp), None) == -1
+    # grad_acc overlapping the master: rejected
+    assert L.zero_reduce_scatter_adam(g, _w(1), 1, 1024, 1, P, M, V, B, _pp(0x100100), None, C.byref(hp), None) == -1
+    # a rank buffer equal to grad_out == grad_acc: rejected
+    assert L.zero_reduce_scatter_adam(_pp(0x500000), _w(1), 1, 1024, 1, P, M, V, B, acc, acc, C.byref(hp),
+                                      None) == -1

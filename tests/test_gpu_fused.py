@@ -91,3 +91,32 @@ def test_fused_equals_separate_calls_on_the_7b_layer():
     for xa, xb in zip(a.master + a.exp_avg + a.exp_avg_sq + a.grad, b.master + b.exp_avg + b.exp_avg_sq + gb):
         assert torch.equal(xa.view(torch.int32), xb.view(torch.int32))
     assert torch.equal(a.view.view(torch.int16), b.view.view(torch.int16))
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+def test_fused_with_accumulator(in_place):
+    # the last micro-batch of an accumulation: grad = acc + red, then update;
+    # equal to the reduce kernel's accumulate mode followed by the update
+    n, per_shard = 4, 4096 + 4
+    numel = n * per_shard
+    grads = S.host_rank_grads(7300, n, numel)
+    w = oracle.weights_mean(n)
+    rng = np.random.default_rng(7301)
+    acc = [S.normal_f32(rng, per_shard, 3e-3) for _ in range(n)]
+    p, m, v = S.host_state(7302, numel, 0.02, 1e-4, 1e-6)
+    sl = [slice(k * per_shard, (k + 1) * per_shard) for k in range(n)]
+    P = [f32_to_dev(p[s]) for s in sl]
+    M = [f32_to_dev(m[s]) for s in sl]
+    V = [f32_to_dev(v[s]) for s in sl]
+    B = [torch.empty(per_shard, dtype=torch.bfloat16, device="cuda") for _ in sl]
+    A = [f32_to_dev(a) for a in acc]
+    G = A if in_place else [torch.empty(per_shard, dtype=torch.float32, device="cuda") for _ in sl]
+    hp = _hp(0.1, 7)
+    z.zero_reduce_scatter_adam([bf16_to_dev(g) for g in grads], w, P, M, V, B, hp, grad_out=G, grad_acc=A)
+    sc = _sc(hp)
+    for k, s in enumerate(sl):
+        tot = acc[k] + oracle.reduce_owner_shard(grads, w, n, k)
+        assert_grad_exact(f32_to_host(G[k]), tot, f"owner {k}")
+        ref = oracle.adam_step(p[s], m[s], v[s], tot, sc)
+        assert_state_close(f32_to_host(P[k]), f32_to_host(M[k]), f32_to_host(V[k]), bf16_to_host(B[k]), ref,
+                           f"owner {k}")

@@ -163,7 +163,8 @@ def test_zero3_chain_full_size():
             assert_state_close(*got, got_b, ref, f"unit {u} window {a}")
 
 
-def test_offload_full_size():
+@pytest.mark.parametrize("fuse_last", [False, True])
+def test_offload_full_size(fuse_last):
     wl = OFFLOAD_8B
     n, M, C = wl.n_ranks, wl.extra["micro_batches"], wl.extra["chunk"]
     st = OffloadStep(wl.psi, n, C, device="cuda")
@@ -186,7 +187,7 @@ def test_offload_full_size():
     def produce(mb, c, views):
         fill.offload_contrib(gen, wl, mb, c, views, tmp)
 
-    st.step(produce, M, w, hp)
+    st.step(produce, M, w, hp, fuse_last=fuse_last)
     st.sync()
     torch.cuda.synchronize()
     host = st.host.numpy()
@@ -202,7 +203,9 @@ def test_offload_full_size():
         for a, p in zip(wins[c], p0[c]):
             acc = oracle.offload_accumulate([[g[a:a + W] for g in mbg] for mbg in per_mb], w)
             lo = c * C + a
-            assert_grad_exact(host[lo:lo + W], acc, f"host shard chunk {c} window {a}")
+            on_host = oracle.offload_accumulate([[g[a:a + W] for g in mbg] for mbg in per_mb[:M - 1]], w) \
+                if fuse_last else acc
+            assert_grad_exact(host[lo:lo + W], on_host, f"host shard chunk {c} window {a}")
             z0 = np.zeros(W, np.float32)
             ref = oracle.adam_step(p, z0, z0.copy(), acc, sc)
             assert_state_close(f32_to_host(st.master[lo:lo + W]), f32_to_host(st.exp_avg[lo:lo + W]),

@@ -5,7 +5,7 @@ The work runs in libzero.so (HIP kernels for gfx950 behind a C ABI, declared
 in include/zero.h); this package is its Python binding and the step drivers
 that sequence its calls.
 """
-from ._lib import ZERO_OFFLOAD_ADAM, ZERO_OFFLOAD_REDUCE, ZeroError, load  # noqa: F401
+from ._lib import ZERO_OFFLOAD_ADAM, ZERO_OFFLOAD_REDUCE, ZERO_OFFLOAD_REDUCE_ADAM, ZeroError, load  # noqa: F401
 from .api import (  # noqa: F401
     ZeroOffload,
     zero_adam_scalars_compute,

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzero.so"
 ZERO_OK, ZERO_ERR_ARG, ZERO_ERR_ALIGN, ZERO_ERR_SIZE, ZERO_ERR_HIP, ZERO_ERR_STATE = 0, -1, -2, -3, -4, -5
 ZERO_MAX_RANKS = 16
 ZERO_NORM_BLOCKS = 1024
-ZERO_OFFLOAD_REDUCE, ZERO_OFFLOAD_ADAM = 0, 1
+ZERO_OFFLOAD_REDUCE, ZERO_OFFLOAD_ADAM, ZERO_OFFLOAD_REDUCE_ADAM = 0, 1, 2
 
 
 class AdamHparams(C.Structure):
@@ -43,7 +43,7 @@ SIGNATURES = {
     "zero_adam_shard_step": (C.c_int, [P, P, P, P, P, I64, C.POINTER(AdamHparams), P]),
     "zero_adam_shard_step_scaled": (C.c_int, [P, P, P, P, P, P, I64, C.POINTER(AdamHparams), P]),
     "zero_grad_norm_sq": (C.c_int, [PP, C.c_int, I64, P, I64, P, C.c_float, P, P]),
-    "zero_reduce_scatter_adam": (C.c_int, [PP, FP, C.c_int, I64, C.c_int, PP, PP, PP, PP, PP,
+    "zero_reduce_scatter_adam": (C.c_int, [PP, FP, C.c_int, I64, C.c_int, PP, PP, PP, PP, PP, PP,
                                            C.POINTER(AdamHparams), P]),
     "zero_all_gather_layer": (C.c_int, [PP, C.c_int, I64, P, P]),
     "zero_offload_create": (C.c_int, [C.c_int, I64, I64, P, PP, PP, C.POINTER(C.c_void_p)]),

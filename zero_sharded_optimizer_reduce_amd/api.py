@@ -163,11 +163,12 @@ def zero_grad_norm_sq(shards: Sequence[torch.Tensor], workspace: torch.Tensor, n
 
 
 def zero_reduce_scatter_adam(rank_grads: Sequence[torch.Tensor], rank_weights, master, exp_avg, exp_avg_sq,
-                             bf16_out, hp, grad_out=None, stream=None) -> None:
+                             bf16_out, hp, grad_out=None, grad_acc=None, stream=None) -> None:
     """Fused reduce-scatter + owner Adam update: for each owner k, the reduced
-    shard k of the rank contributions updates (master[k], exp_avg[k],
-    exp_avg_sq[k]) and writes bf16_out[k]; grad_out (optional list) receives
-    the reduced shards.  Bit-identical to zero_reduce_scatter followed by
+    shard k of the rank contributions (plus grad_acc[k] when given) updates
+    (master[k], exp_avg[k], exp_avg_sq[k]) and writes bf16_out[k]; grad_out
+    (optional list) receives the gradient used.  Bit-identical to
+    zero_reduce_scatter (accumulate mode with grad_acc) followed by
     zero_adam_shard_step on every owner."""
     n_ranks, n_shards = len(rank_grads), len(master)
     if n_ranks < 1 or n_shards < 1:
@@ -190,12 +191,17 @@ def zero_reduce_scatter_adam(rank_grads: Sequence[torch.Tensor], rank_weights, m
         if len(grad_out) != n_shards or any(t.numel() != s for t in grad_out):
             raise ValueError("zero_reduce_scatter_adam: grad_out needs one tensor per owner")
         go = _ptrs([_dev(t, f"grad_out[{k}]", (torch.float32,)) for k, t in enumerate(grad_out)])
+    ga = None
+    if grad_acc is not None:
+        if len(grad_acc) != n_shards or any(t.numel() != s for t in grad_acc):
+            raise ValueError("zero_reduce_scatter_adam: grad_acc needs one tensor per owner")
+        ga = _ptrs([_dev(t, f"grad_acc[{k}]", (torch.float32,)) for k, t in enumerate(grad_acc)])
     w = np.ascontiguousarray(np.asarray(rank_weights, dtype=np.float32))
     if w.size != n_ranks:
         raise ValueError("zero_reduce_scatter_adam: one weight per rank")
     h = hparams(hp)
     check(load().zero_reduce_scatter_adam(_ptrs(gp), w.ctypes.data_as(_lib.FP), n_ranks, numel, n_shards,
-                                          *tables, go, C.byref(h), _stream(stream)),
+                                          *tables, ga, go, C.byref(h), _stream(stream)),
           "zero_reduce_scatter_adam")
 
 
@@ -270,6 +276,22 @@ class ZeroOffload:
         check(load().zero_offload_stream(self._h, _lib.ZERO_OFFLOAD_ADAM, chunk, 0, None, *ptrs,
                                          C.byref(h), _stream(stream)), "zero_offload_stream(ADAM)")
 
+    def reduce_adam(self, chunk: int, micro_batch: int, rank_weights, master, exp_avg, exp_avg_sq, bf16_out, hp,
+                    stream=None) -> None:
+        """The last micro-batch of `chunk`: reduce, add to the host accumulation
+        and update in one pass (no copy back to the host)."""
+        w = np.ascontiguousarray(np.asarray(rank_weights, dtype=np.float32))
+        if w.size != self.n_ranks:
+            raise ValueError("one weight per rank")
+        ptrs = [_dev(master, "master", (torch.float32,)), _dev(exp_avg, "exp_avg", (torch.float32,)),
+                _dev(exp_avg_sq, "exp_avg_sq", (torch.float32,)), _dev(bf16_out, "bf16_out", _BF16_LIKE)]
+        if any(t.numel() != self.shard_numel for t in (master, exp_avg, exp_avg_sq, bf16_out)):
+            raise ValueError("state tensors must cover the whole shard")
+        h = hparams(hp)
+        check(load().zero_offload_stream(self._h, _lib.ZERO_OFFLOAD_REDUCE_ADAM, chunk, micro_batch,
+                                         w.ctypes.data_as(_lib.FP), *ptrs, C.byref(h), _stream(stream)),
+              "zero_offload_stream(REDUCE_ADAM)")
+
     def sync(self) -> None:
         check(load().zero_offload_sync(self._h), "zero_offload_sync")
 
@@ -294,6 +316,8 @@ def zero_offload_stream(h: ZeroOffload, op: int, chunk: int, micro_batch: int = 
                         master=None, exp_avg=None, exp_avg_sq=None, bf16_out=None, hp=None, stream=None):
     if op == _lib.ZERO_OFFLOAD_REDUCE:
         return h.reduce(chunk, micro_batch, rank_weights, stream)
+    if op == _lib.ZERO_OFFLOAD_REDUCE_ADAM:
+        return h.reduce_adam(chunk, micro_batch, rank_weights, master, exp_avg, exp_avg_sq, bf16_out, hp, stream)
     return h.adam(chunk, master, exp_avg, exp_avg_sq, bf16_out, hp, stream)
 
 

@@ -52,6 +52,7 @@ struct FusedParams {
   float* v[ZERO_MAX_RANKS];
   uint16_t* b[ZERO_MAX_RANKS];
   float* gout[ZERO_MAX_RANKS];        // per owner: reduced gradient out, or all NULL
+  const float* gacc[ZERO_MAX_RANKS];  // per owner: accumulator added to the reduction, or all NULL
   int64_t shard;
   int n_ranks;
   zero_adam_scalars s;

@@ -340,10 +340,12 @@ __global__ __launch_bounds__(kBlock) void norm_final_kernel(NormParams p) {
 // the reduce-scatter and the all-gather).  The reduced gradient is formed in
 // registers with exactly the reduce-scatter kernel's arithmetic and handed to
 // the same update, so the results are bit-identical to the two kernels run
-// one after the other; it is written out only when gout is given.  Bytes per
-// parameter (N=4): 8 (contributions) + 12 (state) read, 12 (state) + 2 (BF16)
-// written = 34, against 12 + 30 = 42 for the two kernels.
-template <int N, bool WD, bool WG, int U>
+// one after the other; it is written out only when gout is given.  ACC: the
+// gradient is gacc + red (the reduce kernel's accumulate mode: the last
+// micro-batch of an accumulation updates directly).  Bytes per parameter
+// (N=4): 8 (contributions) + 12 (state) read, 12 (state) + 2 (BF16) written
+// = 34, against 12 + 30 = 42 for the two kernels.
+template <int N, bool WD, bool WG, bool ACC, int U>
 __global__ __launch_bounds__(kBlock) void fused_vec_kernel(FusedParams p) {
   constexpr int NMAX = N > 0 ? N : ZERO_MAX_RANKS;
   const int n = N > 0 ? N : p.n_ranks;
@@ -355,11 +357,12 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(FusedParams p) {
   f32x4* __restrict__ V = reinterpret_cast<f32x4*>(p.v[k]);
   u32x2* __restrict__ B = reinterpret_cast<u32x2*>(p.b[k]);
   f32x4* __restrict__ GO = reinterpret_cast<f32x4*>(p.gout[k]);
+  const f32x4* __restrict__ GA = reinterpret_cast<const f32x4*>(p.gacc[k]);
   const int64_t step = static_cast<int64_t>(gridDim.x) * kBlock * U;
   for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock * U + threadIdx.x; base < nvec;
        base += step) {
     u32x2 x[U][NMAX];
-    f32x4 pv[U], mv[U], vv[U];
+    f32x4 pv[U], mv[U], vv[U], av[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = base + u * kBlock;
@@ -370,13 +373,15 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(FusedParams p) {
         pv[u] = ld_nt(P + i);
         mv[u] = ld_nt(M + i);
         vv[u] = ld_nt(V + i);
+        if (ACC) av[u] = ld_nt(GA + i);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = base + u * kBlock;
       if (i >= nvec) break;
-      const f32x4 g = reduce4<NMAX>(x[u], n, p.w);
+      f32x4 g = reduce4<NMAX>(x[u], n, p.w);
+      if (ACC) g = av[u] + g;
       if (WG) st_nt(g, GO + i);
       float pe[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
       float me[4] = {mv[u].x, mv[u].y, mv[u].z, mv[u].w};
@@ -400,6 +405,7 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(FusedParams p) {
        i += static_cast<int64_t>(gridDim.x) * kBlock) {
     float g = p.w[0] * bf16_at(p.g[0], base + i);
     for (int r = 1; r < p.n_ranks; ++r) g = g + p.w[r] * bf16_at(p.g[r], base + i);
+    if (p.gacc[k]) g = p.gacc[k][i] + g;
     if (p.gout[k]) p.gout[k][i] = g;
     float pe = p.p[k][i], me = p.m[k][i], ve = p.v[k][i];
     adam_elem<WD>(pe, me, ve, g, p.s);
@@ -547,22 +553,27 @@ hipError_t launch_reduce_scatter_f32(const RsParams& p, int n_shards, bool accum
                     : rs_f32_dispatch<false>(p, n_shards, vec, stream);
 }
 
-template <int N, bool WD, bool WG>
+template <int N, bool WD, bool WG, bool ACC>
 hipError_t fused_vec_launch(const FusedParams& p, int n_shards, hipStream_t s) {
   dim3 grid(grid_x(p.shard >> 2, kFusedU, n_shards), n_shards);
-  hipLaunchKernelGGL((fused_vec_kernel<N, WD, WG, kFusedU>), grid, dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL((fused_vec_kernel<N, WD, WG, ACC, kFusedU>), grid, dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 
-template <bool WD, bool WG>
+template <bool WD, bool WG, bool ACC>
 hipError_t fused_dispatch_n(const FusedParams& p, int n_shards, hipStream_t s) {
   switch (p.n_ranks) {
-    case 1: return fused_vec_launch<1, WD, WG>(p, n_shards, s);
-    case 2: return fused_vec_launch<2, WD, WG>(p, n_shards, s);
-    case 4: return fused_vec_launch<4, WD, WG>(p, n_shards, s);
-    case 8: return fused_vec_launch<8, WD, WG>(p, n_shards, s);
-    default: return fused_vec_launch<0, WD, WG>(p, n_shards, s);
+    case 1: return fused_vec_launch<1, WD, WG, ACC>(p, n_shards, s);
+    case 2: return fused_vec_launch<2, WD, WG, ACC>(p, n_shards, s);
+    case 4: return fused_vec_launch<4, WD, WG, ACC>(p, n_shards, s);
+    case 8: return fused_vec_launch<8, WD, WG, ACC>(p, n_shards, s);
+    default: return fused_vec_launch<0, WD, WG, ACC>(p, n_shards, s);
   }
+}
+
+template <bool WD, bool WG>
+hipError_t fused_dispatch_acc(const FusedParams& p, int n_shards, bool acc, hipStream_t s) {
+  return acc ? fused_dispatch_n<WD, WG, true>(p, n_shards, s) : fused_dispatch_n<WD, WG, false>(p, n_shards, s);
 }
 
 hipError_t launch_fused(const FusedParams& p, int n_shards, bool write_grad, bool vec, hipStream_t s) {
@@ -575,8 +586,12 @@ hipError_t launch_fused(const FusedParams& p, int n_shards, bool write_grad, boo
       hipLaunchKernelGGL((fused_scalar_kernel<false>), grid, dim3(kBlock), 0, s, p);
     return hipGetLastError();
   }
-  if (wd) return write_grad ? fused_dispatch_n<true, true>(p, n_shards, s) : fused_dispatch_n<true, false>(p, n_shards, s);
-  return write_grad ? fused_dispatch_n<false, true>(p, n_shards, s) : fused_dispatch_n<false, false>(p, n_shards, s);
+  const bool acc = p.gacc[0] != nullptr;
+  if (wd)
+    return write_grad ? fused_dispatch_acc<true, true>(p, n_shards, acc, s)
+                      : fused_dispatch_acc<true, false>(p, n_shards, acc, s);
+  return write_grad ? fused_dispatch_acc<false, true>(p, n_shards, acc, s)
+                    : fused_dispatch_acc<false, false>(p, n_shards, acc, s);
 }
 
 template <bool WD, bool SC>

@@ -175,7 +175,7 @@ int zero_offload_stream(zero_offload* h, int op, int64_t chunk, int micro_batch,
                         float* exp_avg_sq, uint16_t* bf16_out, const zero_adam_hparams* hp,
                         void* compute_stream) {
   if (!h) return fail(ZERO_ERR_ARG, "offload_stream: NULL handle");
-  if (op != ZERO_OFFLOAD_REDUCE && op != ZERO_OFFLOAD_ADAM)
+  if (op != ZERO_OFFLOAD_REDUCE && op != ZERO_OFFLOAD_ADAM && op != ZERO_OFFLOAD_REDUCE_ADAM)
     return fail(ZERO_ERR_ARG, "offload_stream: unknown op");
   if (chunk < 0 || chunk >= h->n_chunks) return fail(ZERO_ERR_STATE, "offload_stream: chunk out of range");
   int st = check_device(h);
@@ -228,6 +228,54 @@ int zero_offload_stream(zero_offload* h, int op, int64_t chunk, int micro_batch,
     ZCHK(record(h->d2h_done[s], h->d2h));
     ZCHK(record(h->host_written[chunk], h->d2h));
     h->last_mb[chunk] = micro_batch;
+    return ZERO_OK;
+  }
+
+  if (op == ZERO_OFFLOAD_REDUCE_ADAM) {
+    // the last micro-batch, reduced and applied in one pass; its sum never
+    // goes to the host
+    if (micro_batch < 0) return fail(ZERO_ERR_ARG, "offload_stream: micro_batch < 0");
+    if (micro_batch > 0 && h->last_mb[chunk] != micro_batch - 1)
+      return fail(ZERO_ERR_STATE, "offload_stream: micro-batch out of order for this chunk");
+    if (!rank_weights || !master || !exp_avg || !exp_avg_sq || !bf16_out)
+      return fail(ZERO_ERR_ARG, "offload_stream: NULL weights or state pointer");
+    const uint16_t* g[ZERO_MAX_RANKS];
+    for (int r = 0; r < h->n_ranks; ++r) g[r] = h->contrib[s] + r * h->chunk;
+    float* pm[1] = {master + off};
+    float* mm[1] = {exp_avg + off};
+    float* vm[1] = {exp_avg_sq + off};
+    uint16_t* bm[1] = {bf16_out + off};
+    const float* acc[1] = {h->stage[s]};
+    Err e;
+    st = check_reduce_scatter_adam(g, rank_weights, h->n_ranks, len, 1, pm, mm, vm, bm,
+                                   micro_batch > 0 ? acc : nullptr, nullptr, hp, e);
+    if (st) return fail(st, e.msg);
+    if (micro_batch > 0) {
+      st = stream_in(h, chunk, s, len, cs);
+      if (st) return st;
+    }
+    FusedParams p;
+    memset(&p, 0, sizeof p);
+    p.shard = len;
+    p.n_ranks = h->n_ranks;
+    adam_scalars(hp, &p.s, e);
+    bool vec = (len % 4) == 0;
+    for (int r = 0; r < h->n_ranks; ++r) {
+      p.g[r] = g[r];
+      p.w[r] = rank_weights[r];
+      vec = vec && aligned8(g[r]);
+    }
+    p.p[0] = pm[0];
+    p.m[0] = mm[0];
+    p.v[0] = vm[0];
+    p.b[0] = bm[0];
+    p.gacc[0] = micro_batch > 0 ? h->stage[s] : nullptr;
+    vec = vec && aligned16(p.p[0]) && aligned16(p.m[0]) && aligned16(p.v[0]) && aligned8(p.b[0]) &&
+          aligned16(p.gacc[0]);
+    set_path(vec);
+    ZCHK(launch_fused(p, 1, false, vec, cs));
+    ZCHK(record(h->kernel_done[s], cs));
+    h->last_mb[chunk] = -1;   // the accumulation of this chunk is consumed
     return ZERO_OK;
   }
 

@@ -74,8 +74,8 @@ int check_reduce_scatter(const void* const* rank_grads, const float* rank_weight
 int check_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* rank_weights,
                               int n_ranks, int64_t numel, int n_shards, float* const* master,
                               float* const* exp_avg, float* const* exp_avg_sq,
-                              uint16_t* const* bf16_out, float* const* grad_out,
-                              const zero_adam_hparams* hp, Err& e) {
+                              uint16_t* const* bf16_out, const float* const* grad_acc,
+                              float* const* grad_out, const zero_adam_hparams* hp, Err& e) {
   int st = check_adam_hparams(hp, e);
   if (st) return st;
   if (!rank_grads || !rank_weights || !master || !exp_avg || !exp_avg_sq || !bf16_out)
@@ -91,34 +91,61 @@ int check_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* ra
   if (mul_overflows(numel, 4)) return set_err(e, ZERO_ERR_SIZE, "reduce_scatter_adam: numel too large");
   if (numel == 0) return ZERO_OK;
   const int64_t shard = numel / n_shards;
-  Range rs[ZERO_MAX_RANKS * 6];
-  int nr = 0;
+  // outputs: per owner master, m, v, bf16 and (optionally) grad_out; inputs:
+  // the rank contributions and the accumulators.  acc_of_out[i] / acc_of_in[j]
+  // name the owner whose grad_out / grad_acc the range is (-1 otherwise).
+  Range outs[ZERO_MAX_RANKS * 5], ins[ZERO_MAX_RANKS * 2];
+  int out_owner[ZERO_MAX_RANKS * 5], in_owner[ZERO_MAX_RANKS * 2];
+  int no = 0, ni = 0;
   for (int r = 0; r < n_ranks; ++r) {
     if (!rank_grads[r]) return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: rank_grads[%d] is NULL", r);
     if (reinterpret_cast<uintptr_t>(rank_grads[r]) & 1u)
       return set_err(e, ZERO_ERR_ALIGN, "reduce_scatter_adam: rank_grads[%d] not 2-byte aligned", r);
+    in_owner[ni] = -1;
+    ins[ni++] = range_of(rank_grads[r], numel * 2);
   }
   for (int k = 0; k < n_shards; ++k) {
-    const void* f32s[4] = {master[k], exp_avg[k], exp_avg_sq[k], grad_out ? grad_out[k] : nullptr};
-    for (int j = 0; j < 4; ++j) {
-      if (j < 3 && !f32s[j]) return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: NULL state of owner %d", k);
-      if (j == 3 && grad_out && !f32s[j])
-        return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: grad_out[%d] is NULL", k);
-      if (reinterpret_cast<uintptr_t>(f32s[j]) & 3u)
-        return set_err(e, ZERO_ERR_ALIGN, "reduce_scatter_adam: FP32 buffer of owner %d misaligned", k);
-      if (f32s[j]) rs[nr++] = range_of(f32s[j], shard * 4);
+    const void* f32s[3] = {master[k], exp_avg[k], exp_avg_sq[k]};
+    for (const void* q : f32s) {
+      if (!q) return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: NULL state of owner %d", k);
+      if (reinterpret_cast<uintptr_t>(q) & 3u)
+        return set_err(e, ZERO_ERR_ALIGN, "reduce_scatter_adam: FP32 state of owner %d misaligned", k);
+      out_owner[no] = -1;
+      outs[no++] = range_of(q, shard * 4);
     }
     if (!bf16_out[k]) return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: bf16_out[%d] is NULL", k);
     if (reinterpret_cast<uintptr_t>(bf16_out[k]) & 1u)
       return set_err(e, ZERO_ERR_ALIGN, "reduce_scatter_adam: bf16_out[%d] misaligned", k);
-    rs[nr++] = range_of(bf16_out[k], shard * 2);
+    out_owner[no] = -1;
+    outs[no++] = range_of(bf16_out[k], shard * 2);
+    if (grad_out) {
+      if (!grad_out[k]) return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: grad_out[%d] is NULL", k);
+      if (reinterpret_cast<uintptr_t>(grad_out[k]) & 3u)
+        return set_err(e, ZERO_ERR_ALIGN, "reduce_scatter_adam: grad_out[%d] misaligned", k);
+      out_owner[no] = k;
+      outs[no++] = range_of(grad_out[k], shard * 4);
+    }
+    if (grad_acc) {
+      if (!grad_acc[k]) return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: grad_acc[%d] is NULL", k);
+      if (reinterpret_cast<uintptr_t>(grad_acc[k]) & 3u)
+        return set_err(e, ZERO_ERR_ALIGN, "reduce_scatter_adam: grad_acc[%d] misaligned", k);
+      in_owner[ni] = k;
+      ins[ni++] = range_of(grad_acc[k], shard * 4);
+    }
   }
-  const int n_out = nr;
-  for (int r = 0; r < n_ranks; ++r) rs[nr++] = range_of(rank_grads[r], numel * 2);
-  for (int i = 0; i < n_out; ++i)
-    for (int j = i + 1; j < nr; ++j)
-      if (overlaps(rs[i], rs[j]))
-        return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: an output buffer overlaps another buffer");
+  for (int i = 0; i < no; ++i) {
+    for (int j = i + 1; j < no; ++j)
+      if (overlaps(outs[i], outs[j]))
+        return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: two output buffers overlap");
+    for (int j = 0; j < ni; ++j) {
+      // the one permitted alias: grad_out[k] == grad_acc[k] exactly (each
+      // element is read, then written, by the same lane)
+      const bool in_place = out_owner[i] >= 0 && out_owner[i] == in_owner[j] &&
+                            outs[i].lo == ins[j].lo && outs[i].hi == ins[j].hi;
+      if (!in_place && overlaps(outs[i], ins[j]))
+        return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: an output overlaps an input");
+    }
+  }
   return ZERO_OK;
 }
 

@@ -52,8 +52,8 @@ int shard_layout(const int64_t* numels, int n_tensors, int n_shards, int64_t* ps
 int check_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* rank_weights,
                               int n_ranks, int64_t numel, int n_shards, float* const* master,
                               float* const* exp_avg, float* const* exp_avg_sq,
-                              uint16_t* const* bf16_out, float* const* grad_out,
-                              const zero_adam_hparams* hp, Err& e);
+                              uint16_t* const* bf16_out, const float* const* grad_acc,
+                              float* const* grad_out, const zero_adam_hparams* hp, Err& e);
 
 int check_grad_norm(const float* const* shards, int n_shards, int64_t shard_numel,
                     const double* workspace, int64_t workspace_len, const double* norm_sq_out,

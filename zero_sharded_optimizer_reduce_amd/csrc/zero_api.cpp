@@ -190,11 +190,11 @@ int zero_grad_norm_sq(const float* const* shards, int n_shards, int64_t shard_nu
 int zero_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* rank_weights,
                              int n_ranks, int64_t numel, int n_shards, float* const* master,
                              float* const* exp_avg, float* const* exp_avg_sq,
-                             uint16_t* const* bf16_out, float* const* grad_out,
-                             const zero_adam_hparams* hp, void* stream) {
+                             uint16_t* const* bf16_out, const float* const* grad_acc,
+                             float* const* grad_out, const zero_adam_hparams* hp, void* stream) {
   Err e;
   int st = check_reduce_scatter_adam(rank_grads, rank_weights, n_ranks, numel, n_shards, master,
-                                     exp_avg, exp_avg_sq, bf16_out, grad_out, hp, e);
+                                     exp_avg, exp_avg_sq, bf16_out, grad_acc, grad_out, hp, e);
   if (st) return fail(st, e.msg);
   if (numel == 0) return ZERO_OK;
   FusedParams p;
@@ -214,8 +214,9 @@ int zero_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* ran
     p.v[k] = exp_avg_sq[k];
     p.b[k] = bf16_out[k];
     p.gout[k] = grad_out ? grad_out[k] : nullptr;
+    p.gacc[k] = grad_acc ? grad_acc[k] : nullptr;
     vec = vec && aligned16(p.p[k]) && aligned16(p.m[k]) && aligned16(p.v[k]) && aligned8(p.b[k]) &&
-          aligned16(p.gout[k]);
+          aligned16(p.gout[k]) && aligned16(p.gacc[k]);
   }
   set_path(vec);
   return hip_status(launch_fused(p, n_shards, grad_out != nullptr, vec, static_cast<hipStream_t>(stream)),

@@ -181,15 +181,23 @@ class OffloadStep:
         L = self.chunk_len(c)
         return [slot[r * self.chunk: r * self.chunk + L] for r in range(self.n)]
 
-    def step(self, produce, n_micro: int, weights, hp, stream=None):
+    def step(self, produce, n_micro: int, weights, hp, stream=None, fuse_last: bool = False):
         """produce(mb, c, views) writes chunk c's contributions for micro-batch
-        mb into `views` on the current stream."""
+        mb into `views` on the current stream.  fuse_last: the last
+        micro-batch's reduction is applied directly (REDUCE_ADAM) instead of
+        going to the host and streaming back (ADAM)."""
         for mb in range(n_micro):
+            last = fuse_last and mb == n_micro - 1
             for c in range(self.n_chunks):
                 produce(mb, c, self.contrib_views(c))
-                self.engine.reduce(c, mb, weights, stream)
-        for c in range(self.n_chunks):
-            self.engine.adam(c, self.master, self.exp_avg, self.exp_avg_sq, self.bf16, hp, stream)
+                if last:
+                    self.engine.reduce_adam(c, mb, weights, self.master, self.exp_avg, self.exp_avg_sq,
+                                            self.bf16, hp, stream)
+                else:
+                    self.engine.reduce(c, mb, weights, stream)
+        if not fuse_last:
+            for c in range(self.n_chunks):
+                self.engine.adam(c, self.master, self.exp_avg, self.exp_avg_sq, self.bf16, hp, stream)
 
     def sync(self):
         self.engine.sync()
