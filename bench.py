@@ -107,6 +107,27 @@ class Timer:
         return float(sum(a.elapsed_time(b) for a, b in self.spans.get(name, [])))
 
 
+def copy_ceiling_gbs(nbytes=1 << 30, reps=20):
+    """Same-run ceiling: the library's copy kernel (all-gather of one shard)
+    over nbytes, read + write bytes per second."""
+    import torch
+
+    import zero_sharded_optimizer_reduce_amd as z
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        z.zero_all_gather_layer([src], dst)
+    T = Timer()
+    a = T.ev()
+    for _ in range(reps):
+        z.zero_all_gather_layer([src], dst)
+    b = T.ev()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def _base(workload_desc, value, ms_step, args, extra_cfg=None):
     cfg = {"workload": workload_desc}
     cfg.update(extra_cfg or {})
@@ -238,6 +259,7 @@ def run_flat(args, wl, numels, grad_scales=None, counts=None, steps_are_adam_t=T
                          "gbs": (2 * n + 26) * pad / (fk * 1e-3) / 1e9},
         "hbm_gbs_algorithmic": (2 * n + 26 + B_AG) * pad / (f_ms * 1e-3) / 1e9,
     }
+    out["copy_ceiling_gbs_same_run"] = copy_ceiling_gbs()
     return out
 
 
@@ -310,6 +332,27 @@ def run_owner_share(args):
                     "adam_shard_step": {"ms": adam_ms, "bytes": B_ADAM * B, "gbs": B_ADAM * B / (adam_ms * 1e-3) / 1e9}},
         "roofline": _roofline("adam_shard_step", wl.name, adam_ms, B),
     })
+    # the same step with the fused reduce + update kernel per bucket (34 B/param)
+    torch.cuda.synchronize()
+    start = T.ev()
+    for _ in range(args.steps):
+        t += 1
+        hp = wl.hparams(step=t)
+        for b, (lo, hi) in enumerate(st.bounds):
+            a = T.ev()
+            z.zero_reduce_scatter_adam([c[lo:hi] for c in st.contrib], w, [st.master[lo:hi]], [st.exp_avg[lo:hi]],
+                                       [st.exp_avg_sq[lo:hi]], [st.bf16[lo:hi]], hp)
+            if hi - lo == st.bucket:
+                T.span("fused", a, T.ev())
+    stop = T.ev()
+    torch.cuda.synchronize()
+    f_ms = start.elapsed_time(stop) / args.steps
+    fk = T.ms("fused")
+    out["fused_variant"] = {"ms_per_step": f_ms, "value": wl.psi / (f_ms * 1e-3),
+                            "hbm_gbs_algorithmic": (2 * n + 26) * wl.psi / (f_ms * 1e-3) / 1e9,
+                            "fused_kernel": {"ms": fk, "bytes": (2 * n + 26) * B,
+                                             "gbs": (2 * n + 26) * B / (fk * 1e-3) / 1e9}}
+    out["copy_ceiling_gbs_same_run"] = copy_ceiling_gbs()
     return out
 
 
@@ -336,20 +379,24 @@ def run_chain(args):
     T = Timer()
     U = len(ch.units)
 
-    def step(t, timed):
+    def step(t, timed, fused=False):
         hp = wl.hparams(step=t)
+        pre = "f_" if fused else ""
         for u in range(U):                      # forward: gather, use, release
             a = T.ev() if timed else None
             ch.forward_unit(u)
             if timed:
-                T.span("ag" if u not in (0, U - 1) else "ag_edge", a, T.ev())
+                T.span(pre + "ag", a, T.ev())
         for u in reversed(range(U)):            # backward
             pad = ch.units[u][2]
             fill.chain_unit_grads(gen, wl, u, ch.grads, pad, tmp)   # producer, not timed
             a = T.ev() if timed else None
-            ch.backward_unit(u, w, hp)
+            if fused:
+                ch.backward_unit_fused(u, w, hp)
+            else:
+                ch.backward_unit(u, w, hp)
             if timed:
-                T.span("bwd" if u not in (0, U - 1) else "bwd_edge", a, T.ev())
+                T.span(pre + "bwd", a, T.ev())
 
     torch.cuda.synchronize()
     t = 0
@@ -364,9 +411,14 @@ def run_chain(args):
         step(t, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
-    fwd_ms = (T.total_ms("ag") + T.total_ms("ag_edge")) / args.steps
-    bwd_ms = (T.total_ms("bwd") + T.total_ms("bwd_edge")) / args.steps
+    fwd_ms = T.total_ms("ag") / args.steps
+    bwd_ms = T.total_ms("bwd") / args.steps
     ms_step = fwd_ms + bwd_ms
+    for _ in range(args.steps):
+        t += 1
+        step(t, True, fused=True)
+    torch.cuda.synchronize()
+    f_ms = (T.total_ms("f_ag") + T.total_ms("f_bwd")) / args.steps
     psi_pad = sum(u[2] for u in ch.units)
     step_bytes = (B_RS(n) + B_ADAM + B_AG) * psi_pad
     # kernel-level timing of one layer unit
@@ -404,7 +456,10 @@ def run_chain(args):
                     "adam_shard_step_layer": {"ms": adam_ms, "bytes": B_ADAM * s,
                                               "gbs": B_ADAM * s / (adam_ms * 1e-3) / 1e9}},
         "roofline": _roofline("adam_shard_step", wl.name, adam_ms, s),
+        "fused_variant": {"ms_per_step": f_ms, "value": wl.psi / (f_ms * 1e-3),
+                          "hbm_gbs_algorithmic": (2 * n + 26 + B_AG) * psi_pad / (f_ms * 1e-3) / 1e9},
     })
+    out["copy_ceiling_gbs_same_run"] = copy_ceiling_gbs()
     return out
 
 

@@ -1,0 +1,108 @@
+// Host-only driver for the C ABI's argument checks, built with g++ and the
+// address/undefined-behaviour sanitizers (no HIP, no device).  Exercises every
+// check with valid, boundary and invalid arguments; prints "ok" on success.
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../zero_sharded_optimizer_reduce_amd/csrc/validate.h"
+
+using namespace zero;
+
+static int fails = 0;
+#define EXPECT(cond)                                              \
+  do {                                                            \
+    if (!(cond)) {                                                \
+      std::printf("FAILED line %d: %s\n", __LINE__, #cond);       \
+      ++fails;                                                    \
+    }                                                             \
+  } while (0)
+
+static void* P(uintptr_t a) { return reinterpret_cast<void*>(a); }
+
+int main() {
+  Err e;
+  // reduce-scatter
+  const void* g4[4] = {P(0x10000), P(0x20000), P(0x30000), P(0x40000)};
+  float* o4[4] = {(float*)P(0x100000), (float*)P(0x110000), (float*)P(0x120000), (float*)P(0x130000)};
+  float w4[4] = {0.25f, 0.25f, 0.25f, 0.25f};
+  EXPECT(check_reduce_scatter(g4, w4, 4, 1024, o4, 4, 0, e) == ZERO_OK);
+  EXPECT(check_reduce_scatter(g4, w4, 4, 1024, o4, 4, 1, e, 4) == ZERO_OK);
+  EXPECT(check_reduce_scatter(g4, w4, 0, 1024, o4, 4, 0, e) == ZERO_ERR_ARG);
+  EXPECT(check_reduce_scatter(g4, w4, 4, 1023, o4, 4, 0, e) == ZERO_ERR_SIZE);
+  EXPECT(check_reduce_scatter(g4, w4, 4, INT64_MAX - 3, o4, 4, 0, e) != ZERO_OK);
+  EXPECT(check_reduce_scatter(nullptr, w4, 4, 1024, o4, 4, 0, e) == ZERO_ERR_ARG);
+  const void* gbad[4] = {P(0x10001), P(0x20000), P(0x30000), P(0x40000)};
+  EXPECT(check_reduce_scatter(gbad, w4, 4, 1024, o4, 4, 0, e) == ZERO_ERR_ALIGN);
+  float* oover[4] = {(float*)P(0x10100), (float*)P(0x110000), (float*)P(0x120000), (float*)P(0x130000)};
+  EXPECT(check_reduce_scatter(g4, w4, 4, 1024, oover, 4, 0, e) == ZERO_ERR_ARG);
+  EXPECT(std::strstr(e.msg, "overlap") != nullptr);
+  // Adam
+  zero_adam_hparams hp = {1e-3f, 0.9f, 0.999f, 1e-8f, 0.0f, 1};
+  float* p = (float*)P(0x100000);
+  float* m = (float*)P(0x200000);
+  float* v = (float*)P(0x300000);
+  uint16_t* b = (uint16_t*)P(0x400000);
+  float* gr = (float*)P(0x500000);
+  EXPECT(check_adam(p, m, v, b, gr, 4096, &hp, e) == ZERO_OK);
+  EXPECT(check_adam(p, p + 16, v, b, gr, 4096, &hp, e) == ZERO_ERR_ARG);
+  EXPECT(check_adam(nullptr, nullptr, nullptr, nullptr, nullptr, 0, &hp, e) == ZERO_OK);
+  zero_adam_hparams bad = hp;
+  bad.step = 0;
+  EXPECT(check_adam(p, m, v, b, gr, 16, &bad, e) == ZERO_ERR_ARG);
+  bad = hp;
+  bad.beta2 = 1.0f;
+  EXPECT(check_adam(p, m, v, b, gr, 16, &bad, e) == ZERO_ERR_ARG);
+  // scalars
+  zero_adam_scalars sc;
+  EXPECT(adam_scalars(&hp, &sc, e) == ZERO_OK);
+  EXPECT(sc.bias_correction1 == sc.one_minus_beta1);
+  hp.step = 1000000000000LL;  // bias corrections saturate to 1
+  EXPECT(adam_scalars(&hp, &sc, e) == ZERO_OK && sc.bias_correction1 == 1.0f);
+  // weights and layout
+  int64_t counts[4] = {4096, 3072, 4096, 2048};
+  float w[4];
+  EXPECT(rank_weights(counts, 4, w, e) == ZERO_OK);
+  { float w16[16]; EXPECT(rank_weights(nullptr, 16, w16, e) == ZERO_OK && w16[15] == 0.0625f); }
+  int64_t zeros[2] = {0, 0};
+  EXPECT(rank_weights(zeros, 2, w, e) == ZERO_ERR_ARG);
+  int64_t huge[2] = {INT64_MAX, 5};
+  EXPECT(rank_weights(huge, 2, w, e) == ZERO_ERR_SIZE);
+  int64_t numels[3] = {5, 7, 0};
+  int64_t psi, pad, s;
+  EXPECT(shard_layout(numels, 3, 4, &psi, &pad, &s, e) == ZERO_OK && psi == 12 && pad == 1024 && s == 256);
+  int64_t big[2] = {INT64_MAX / 8, INT64_MAX / 8};
+  EXPECT(shard_layout(big, 2, 4, &psi, &pad, &s, e) == ZERO_ERR_SIZE);
+  // all-gather
+  const void* sh[2] = {P(0x10000), P(0x20000)};
+  EXPECT(check_all_gather(sh, 2, 4096, P(0x100000), e) == ZERO_OK);
+  EXPECT(check_all_gather(sh, 2, 4096, P(0x10800), e) == ZERO_ERR_ARG);
+  // fused
+  const uint16_t* fg[1] = {(const uint16_t*)P(0x10000000)};
+  float* fp[1] = {p};
+  float* fm[1] = {m};
+  float* fv[1] = {v};
+  uint16_t* fb[1] = {b};
+  const float* facc[1] = {gr};
+  float* fout[1] = {gr};
+  hp.step = 3;
+  EXPECT(check_reduce_scatter_adam(fg, w4, 1, 1024, 1, fp, fm, fv, fb, facc, fout, &hp, e) == ZERO_OK);
+  float* fout2[1] = {gr + 4};
+  EXPECT(check_reduce_scatter_adam(fg, w4, 1, 1024, 1, fp, fm, fv, fb, facc, fout2, &hp, e) == ZERO_ERR_ARG);
+  // gradient norm
+  const float* ns[2] = {(const float*)P(0x100000), (const float*)P(0x200000)};
+  double* ws = (double*)P(0x1000000);
+  double* out = (double*)P(0x2000000);
+  EXPECT(check_grad_norm(ns, 2, 4096, ws, 2048, out, 1.0f, nullptr, e) == ZERO_OK);
+  EXPECT(check_grad_norm(ns, 2, 4096, ws, 2047, out, 1.0f, nullptr, e) == ZERO_ERR_SIZE);
+  EXPECT(check_grad_norm(ns, 2, 4096, ws, 2048, out, 0.0f, (float*)P(0x3000000), e) == ZERO_ERR_ARG);
+  // offload
+  uint16_t* slots[2] = {(uint16_t*)P(0x100000), (uint16_t*)P(0x900000)};
+  float* stage[2] = {(float*)P(0x2000000), (float*)P(0x3000000)};
+  EXPECT(check_offload_create(4, 1 << 20, 1 << 18, (const float*)P(0x5000), slots, stage, e) == ZERO_OK);
+  uint16_t* slots_over[2] = {(uint16_t*)P(0x100000), (uint16_t*)P(0x800000)};
+  EXPECT(check_offload_create(4, 1 << 20, 1 << 20, (const float*)P(0x5000), slots_over, stage, e) == ZERO_ERR_ARG);
+  if (fails) return 1;
+  std::printf("ok\n");
+  return 0;
+}

@@ -120,3 +120,32 @@ def test_fused_with_accumulator(in_place):
         ref = oracle.adam_step(p[s], m[s], v[s], tot, sc)
         assert_state_close(f32_to_host(P[k]), f32_to_host(M[k]), f32_to_host(V[k]), bf16_to_host(B[k]), ref,
                            f"owner {k}")
+
+
+def test_chain_backward_fused_equals_separate():
+    from zero_sharded_optimizer_reduce_amd.drivers import Zero3Chain
+    units = [("emb", [("e", 4 * 256 * 7)]), ("layer", [("a", 5000), ("b", 3000)]), ("head", [("h", 4 * 256 * 3)])]
+    n = 4
+    gen = S.DeviceGen(123)
+    chains = [Zero3Chain(units, n), Zero3Chain(units, n)]
+    for ch in chains:
+        for k in range(n):
+            gen.normal_(ch.master[k], 0.02, 1, k)
+            ch.bf16[k].copy_(ch.master[k])
+    w = z.zero_rank_weights([3, 5, 2, 7], n)
+    tmp = torch.empty(chains[0].max_pad, device="cuda")
+    for t in (1, 2):
+        hp = _hp(0.1, t)
+        for u in reversed(range(len(units))):
+            pad = chains[0].units[u][2]
+            for ch in chains:
+                for r, g in enumerate(ch.grads):
+                    gen.bf16_normal_(g[:pad], 1e-3, 50 + t, u, r, tmp=tmp[:pad])
+            chains[0].backward_unit(u, w, hp)
+            chains[1].backward_unit_fused(u, w, hp)
+    torch.cuda.synchronize()
+    a, b = chains
+    for xa, xb in zip(a.master + a.exp_avg + a.exp_avg_sq, b.master + b.exp_avg + b.exp_avg_sq):
+        assert torch.equal(xa.view(torch.int32), xb.view(torch.int32))
+    for xa, xb in zip(a.bf16, b.bf16):
+        assert torch.equal(xa.view(torch.int16), xb.view(torch.int16))

@@ -22,7 +22,7 @@ from typing import Optional, Sequence
 import torch
 
 from .api import (ZeroOffload, zero_adam_shard_step, zero_all_gather_layer, zero_reduce_scatter,
-                  zero_shard_layout)
+                  zero_reduce_scatter_adam, zero_shard_layout)
 
 
 def _empty(n, dtype, device):
@@ -143,6 +143,15 @@ class Zero3Chain:
         view = self.view[:pad]
         zero_all_gather_layer(self.owner_slices(u, self.bf16), view, stream=stream)
         return view
+
+    def backward_unit_fused(self, u: int, weights, hp, stream=None):
+        """backward_unit with the fused reduce-scatter + update kernel (one
+        launch for the 4 owners; the reduced shards are not stored)."""
+        pad = self.units[u][2]
+        zero_reduce_scatter_adam([g[:pad] for g in self.grads], weights,
+                                 *(self.owner_slices(u, x) for x in
+                                   (self.master, self.exp_avg, self.exp_avg_sq, self.bf16)),
+                                 hp, stream=stream)
 
     def backward_unit(self, u: int, weights, hp, stream=None):
         pad, s = self.units[u][2], self.units[u][3]
