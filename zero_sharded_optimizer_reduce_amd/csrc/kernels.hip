@@ -125,28 +125,28 @@ __global__ __launch_bounds__(kBlock) void rs_f32_scalar_kernel(RsParams p) {
   }
 }
 
-template <int N, bool ACC, int U>
-__global__ __launch_bounds__(kBlock) void rs_vec_kernel(RsParams p) {
+template <int N, bool ACC, int U, int BS>
+__global__ __launch_bounds__(BS) void rs_vec_kernel(RsParams p) {
   constexpr int NMAX = N > 0 ? N : ZERO_MAX_RANKS;
   const int n = N > 0 ? N : p.n_ranks;
   const int k = blockIdx.y;
   const int64_t nvec = p.shard >> 2;
   const int64_t off = static_cast<int64_t>(k) * nvec;
   f32x4* __restrict__ out = reinterpret_cast<f32x4*>(p.out[k]);
-  const int64_t step = static_cast<int64_t>(gridDim.x) * kBlock * U;
-  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock * U + threadIdx.x; base < nvec;
+  const int64_t step = static_cast<int64_t>(gridDim.x) * BS * U;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * BS * U + threadIdx.x; base < nvec;
        base += step) {
     u32x2 x[U][NMAX];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t i = base + u * kBlock;
+      const int64_t i = base + u * BS;
 #pragma unroll
       for (int r = 0; r < NMAX; ++r)
         if (r < n && i < nvec) x[u][r] = ld_nt(reinterpret_cast<const u32x2*>(p.g[r]) + off + i);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t i = base + u * kBlock;
+      const int64_t i = base + u * BS;
       if (i >= nvec) break;
       f32x4 a = reduce4<NMAX>(x[u], n, p.w);
       if (ACC) a = out[i] + a;
@@ -194,8 +194,8 @@ __device__ __forceinline__ void adam_elem(float& p, float& m, float& v, float g,
 // weight (14 B/param).  Vector path: 4 elements per 16-byte access, U vectors
 // per lane per iteration; the n % 4 tail goes element-wise.  SC: the gradient
 // is first multiplied by the device scalar *gscale (the clip coefficient).
-template <bool WD, bool SC, int U>
-__global__ __launch_bounds__(kBlock) void adam_vec_kernel(AdamParams a) {
+template <bool WD, bool SC, int U, int BS>
+__global__ __launch_bounds__(BS) void adam_vec_kernel(AdamParams a) {
   const int64_t nvec = a.n >> 2;
   f32x4* __restrict__ P = reinterpret_cast<f32x4*>(a.p);
   f32x4* __restrict__ M = reinterpret_cast<f32x4*>(a.m);
@@ -203,13 +203,13 @@ __global__ __launch_bounds__(kBlock) void adam_vec_kernel(AdamParams a) {
   const f32x4* __restrict__ G = reinterpret_cast<const f32x4*>(a.g);
   u32x2* __restrict__ B = reinterpret_cast<u32x2*>(a.b);
   const float c = SC ? *a.gscale : 1.0f;
-  const int64_t step = static_cast<int64_t>(gridDim.x) * kBlock * U;
-  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock * U + threadIdx.x; base < nvec;
+  const int64_t step = static_cast<int64_t>(gridDim.x) * BS * U;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * BS * U + threadIdx.x; base < nvec;
        base += step) {
     f32x4 g[U], p[U], m[U], v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t i = base + u * kBlock;
+      const int64_t i = base + u * BS;
       if (i < nvec) {
         g[u] = ld_nt(G + i);
         p[u] = ld_nt(P + i);
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kBlock) void adam_vec_kernel(AdamParams a) {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t i = base + u * kBlock;
+      const int64_t i = base + u * BS;
       if (i >= nvec) break;
       if (SC) g[u] = g[u] * c;
       float pe[4] = {p[u].x, p[u].y, p[u].z, p[u].w};
@@ -419,22 +419,22 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(FusedParams p) {
 // ---------------------------------------------------------------- all-gather
 // The full view is the owners' shards concatenated in owner order (essay,
 // section ZeRO-3 的一次完整计算; slide, note 原 N47).  Owner k = blockIdx.y.
-template <typename T, int U>
-__global__ __launch_bounds__(kBlock) void gather_kernel(GatherParams p) {
+template <typename T, int U, int BS>
+__global__ __launch_bounds__(BS) void gather_kernel(GatherParams p) {
   const int k = blockIdx.y;
   const int64_t n = p.shard_bytes / static_cast<int64_t>(sizeof(T));
   const T* __restrict__ src = reinterpret_cast<const T*>(p.src[k]);
   T* __restrict__ dst = reinterpret_cast<T*>(static_cast<char*>(p.dst) + k * p.shard_bytes);
-  const int64_t step = static_cast<int64_t>(gridDim.x) * kBlock * U;
-  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock * U + threadIdx.x; base < n;
+  const int64_t step = static_cast<int64_t>(gridDim.x) * BS * U;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * BS * U + threadIdx.x; base < n;
        base += step) {
     T x[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (base + u * kBlock < n) x[u] = ld_nt(src + base + u * kBlock);
+      if (base + u * BS < n) x[u] = ld_nt(src + base + u * BS);
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (base + u * kBlock < n) st_nt(x[u], dst + base + u * kBlock);
+      if (base + u * BS < n) st_nt(x[u], dst + base + u * BS);
   }
 }
 
@@ -479,8 +479,8 @@ int device_cus() {
 
 // Blocks along x for `units` work items per owner, each block covering
 // kBlock*u of them per loop iteration.
-unsigned grid_x(int64_t units, int u, int n_y) {
-  const int64_t per_iter = static_cast<int64_t>(kBlock) * u;
+unsigned grid_x(int64_t units, int u, int n_y, int bs = kBlock) {
+  const int64_t per_iter = static_cast<int64_t>(bs) * u;
   int64_t need = (units + per_iter - 1) / per_iter;
   int64_t cap = kMaxGridX;
   if (blocks_per_cu() > 0) cap = static_cast<int64_t>(device_cus()) * blocks_per_cu() / (n_y > 0 ? n_y : 1);
@@ -489,6 +489,12 @@ unsigned grid_x(int64_t units, int u, int n_y) {
   if (need < 1) need = 1;
   return static_cast<unsigned>(need);
 }
+
+// Workgroup sizes of the streaming kernels, chosen by same-box A/B runs on
+// MI355X (256 is used where the size made no measurable difference).
+constexpr int kRsBlock = 128;
+constexpr int kAdamBlock = 128;
+constexpr int kGatherBlock = 64;
 
 // Vectors per lane per loop iteration (measured: 1 is best with full grids).
 constexpr int kRsU = 2;
@@ -511,8 +517,8 @@ template <int N, bool ACC>
 hipError_t rs_vec_launch(const RsParams& p, int n_shards, hipStream_t s) {
   for (int k = 0; k < n_shards; ++k) {
     const RsParams q = owner_slice(p, k, p.shard);
-    dim3 grid(grid_x(p.shard >> 2, kRsU, 1), 1);
-    hipLaunchKernelGGL((rs_vec_kernel<N, ACC, kRsU>), grid, dim3(kBlock), 0, s, q);
+    dim3 grid(grid_x(p.shard >> 2, kRsU, 1, kRsBlock), 1);
+    hipLaunchKernelGGL((rs_vec_kernel<N, ACC, kRsU, kRsBlock>), grid, dim3(kRsBlock), 0, s, q);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -633,8 +639,8 @@ hipError_t launch_fused(const FusedParams& p, int n_shards, bool write_grad, boo
 template <bool WD, bool SC>
 hipError_t adam_launch(const AdamParams& a, bool vec, hipStream_t s) {
   if (vec) {
-    dim3 grid(grid_x(a.n >> 2, kAdamU, 1));
-    hipLaunchKernelGGL((adam_vec_kernel<WD, SC, kAdamU>), grid, dim3(kBlock), 0, s, a);
+    dim3 grid(grid_x(a.n >> 2, kAdamU, 1, kAdamBlock));
+    hipLaunchKernelGGL((adam_vec_kernel<WD, SC, kAdamU, kAdamBlock>), grid, dim3(kAdamBlock), 0, s, a);
   } else {
     dim3 grid(grid_x(a.n, 1, 1));
     hipLaunchKernelGGL((adam_scalar_kernel<WD, SC>), grid, dim3(kBlock), 0, s, a);
@@ -667,15 +673,16 @@ hipError_t launch_norm(NormParams& p, bool vec, hipStream_t s) {
 }
 
 hipError_t launch_gather(const GatherParams& p, int n_shards, int path, hipStream_t s) {
+  constexpr int bs = kGatherBlock;
   if (path == GATHER_V16) {
-    dim3 grid(grid_x(p.shard_bytes / 16, kGatherU, n_shards), n_shards);
-    hipLaunchKernelGGL((gather_kernel<u32x4, kGatherU>), grid, dim3(kBlock), 0, s, p);
+    dim3 grid(grid_x(p.shard_bytes / 16, kGatherU, n_shards, bs), n_shards);
+    hipLaunchKernelGGL((gather_kernel<u32x4, kGatherU, bs>), grid, dim3(bs), 0, s, p);
   } else if (path == GATHER_U32) {
-    dim3 grid(grid_x(p.shard_bytes / 4, kGatherU, n_shards), n_shards);
-    hipLaunchKernelGGL((gather_kernel<uint32_t, kGatherU>), grid, dim3(kBlock), 0, s, p);
+    dim3 grid(grid_x(p.shard_bytes / 4, kGatherU, n_shards, bs), n_shards);
+    hipLaunchKernelGGL((gather_kernel<uint32_t, kGatherU, bs>), grid, dim3(bs), 0, s, p);
   } else {
-    dim3 grid(grid_x(p.shard_bytes, kGatherU, n_shards), n_shards);
-    hipLaunchKernelGGL((gather_kernel<uint8_t, kGatherU>), grid, dim3(kBlock), 0, s, p);
+    dim3 grid(grid_x(p.shard_bytes, kGatherU, n_shards, bs), n_shards);
+    hipLaunchKernelGGL((gather_kernel<uint8_t, kGatherU, bs>), grid, dim3(bs), 0, s, p);
   }
   return hipGetLastError();
 }
