@@ -171,7 +171,15 @@ def cpu_baseline(target_s: float):
 
 
 # --------------------------------------------------------------------------- flat units
-def run_flat(args, wl, numels, grad_scales=None, counts=None, steps_are_adam_t=True):
+SAMPLE_EVERY = 4   # steps between the sampled per-kernel event pairs
+
+
+def run_flat(args, wl, numels, grad_scales=None, counts=None):
+    """Timed region: args.steps steps bracketed by two events, with an event
+    pair around the 4 owner updates on every SAMPLE_EVERY-th step only: an
+    event between two kernels costs about 10 us of GPU time on this stack, so
+    events around every kernel would add about 3% to the step.  The reduce
+    and all-gather durations come from a separate breakdown pass."""
     import torch
 
     import synthetic as S
@@ -191,37 +199,55 @@ def run_flat(args, wl, numels, grad_scales=None, counts=None, steps_are_adam_t=T
     del tmp
     w = z.zero_rank_weights(counts, n)
     T = Timer()
-    torch.cuda.synchronize()
     t = 0
-    for _ in range(args.warmup):
+
+    def timed(step_fn, phase_name):
+        nonlocal t
+        for _ in range(args.warmup):
+            t += 1
+            step_fn(wl.hparams(step=t), None)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start = T.ev()
+        for i in range(args.steps):
+            t += 1
+            step_fn(wl.hparams(step=t), phase_name if i % SAMPLE_EVERY == 0 else None)
+        stop = T.ev()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps, time.perf_counter() - t0
+
+    def sep_step(hp, sample):
+        st.reduce_scatter(grads, w)
+        a = T.ev() if sample else None
+        st.update(hp)
+        if sample:
+            T.span(sample, a, T.ev())
+        st.all_gather()
+
+    def fused_step(hp, sample):
+        a = T.ev() if sample else None
+        z.zero_reduce_scatter_adam(grads, w, st.master, st.exp_avg, st.exp_avg_sq, st.bf16, hp)
+        if sample:
+            T.span(sample, a, T.ev())
+        st.all_gather()
+
+    ms_step, wall = timed(sep_step, "update4")
+    adam_ms = T.ms("update4") / n
+    # breakdown pass for the reduce-scatter and the all-gather (not the timed region)
+    for _ in range(max(4, args.steps // SAMPLE_EVERY)):
         t += 1
-        st.step(grads, w, wl.hparams(step=t))
-    torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    start = T.ev()
-    for _ in range(args.steps):
-        t += 1
-        hp = wl.hparams(step=t)
         a = T.ev()
         st.reduce_scatter(grads, w)
         b = T.ev()
-        T.span("rs", a, b)
-        for k in range(n):
-            a = T.ev()
-            z.zero_adam_shard_step(st.master[k], st.exp_avg[k], st.exp_avg_sq[k], st.bf16[k], st.grad[k], hp)
-            b = T.ev()
-            T.span("adam", a, b)
-        a = T.ev()
+        st.update(wl.hparams(step=t))
+        c = T.ev()
         st.all_gather()
-        b = T.ev()
-        T.span("ag", a, b)
-    stop = T.ev()
+        T.span("rs", a, b)
+        T.span("ag", c, T.ev())
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall0
-    ms_step = start.elapsed_time(stop) / args.steps
     pad = st.psi_pad
     step_bytes = (B_RS(n) + B_ADAM + B_AG) * pad
-    rs_ms, adam_ms, ag_ms = T.ms("rs"), T.ms("adam"), T.ms("ag")
+    rs_ms, ag_ms = T.ms("rs"), T.ms("ag")
     out = _base(wl.description, st.psi / (ms_step * 1e-3), ms_step, args,
                 {"params": st.psi, "n_ranks": n, "storage": "bf16 grads and working weights, fp32 master/m/v",
                  "step": "reduce-scatter + 4 owner Adam updates + all-gather"})
@@ -232,30 +258,21 @@ def run_flat(args, wl, numels, grad_scales=None, counts=None, steps_are_adam_t=T
         "kernels": {
             "reduce_scatter": {"ms": rs_ms, "bytes": B_RS(n) * pad, "gbs": B_RS(n) * pad / (rs_ms * 1e-3) / 1e9},
             "adam_shard_step": {"ms": adam_ms, "bytes": B_ADAM * st.shard,
-                                "gbs": B_ADAM * st.shard / (adam_ms * 1e-3) / 1e9},
+                                "gbs": B_ADAM * st.shard / (adam_ms * 1e-3) / 1e9,
+                                "timing": f"event pair around the 4 owner updates on every {SAMPLE_EVERY}th "
+                                          "timed step, divided by 4"},
             "all_gather": {"ms": ag_ms, "bytes": B_AG * pad, "gbs": B_AG * pad / (ag_ms * 1e-3) / 1e9},
         },
         "roofline": _roofline("adam_shard_step", wl.name, adam_ms, st.shard),
     })
-    # the same step with the fused reduce-scatter + update kernel (one launch
-    # for all owners, reduced gradient kept in registers) and the all-gather
-    torch.cuda.synchronize()
-    start = T.ev()
-    for _ in range(args.steps):
-        t += 1
-        hp = wl.hparams(step=t)
-        a = T.ev()
-        z.zero_reduce_scatter_adam(grads, w, st.master, st.exp_avg, st.exp_avg_sq, st.bf16, hp)
-        T.span("fused", a, T.ev())
-        st.all_gather()
-    stop = T.ev()
-    torch.cuda.synchronize()
-    f_ms = start.elapsed_time(stop) / args.steps
-    fk = T.ms("fused")
+    # the same step with the fused reduce-scatter + update kernel (reduced
+    # gradient kept in registers) and the all-gather
+    f_ms, _ = timed(fused_step, "fused4")
+    fk = T.ms("fused4")
     out["fused_variant"] = {
         "ms_per_step": f_ms, "value": st.psi / (f_ms * 1e-3),
-        "step": "fused reduce-scatter + 4 owner updates (one launch) + all-gather, 38 B/param",
-        "fused_kernel": {"ms": fk, "bytes": (2 * n + 26) * pad,
+        "step": "fused reduce-scatter + owner updates (one launch per owner) + all-gather, 38 B/param",
+        "fused_kernel": {"ms": fk / n, "bytes": (2 * n + 26) * st.shard,
                          "gbs": (2 * n + 26) * pad / (fk * 1e-3) / 1e9},
         "hbm_gbs_algorithmic": (2 * n + 26 + B_AG) * pad / (f_ms * 1e-3) / 1e9,
     }
@@ -293,34 +310,50 @@ def run_owner_share(args):
     del tmp
     w = z.zero_rank_weights(None, n)
     T = Timer()
-    torch.cuda.synchronize()
+    B = st.bucket
     t = wl.step0 - 1
-    for _ in range(args.warmup):
-        t += 1
-        st.step(w, wl.hparams(step=t))
-    torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    start = T.ev()
-    for _ in range(args.steps):
-        t += 1
-        hp = wl.hparams(step=t)
+
+    def sep_step(hp, sample):
         for b, (lo, hi) in enumerate(st.bounds):
             g = st.grad_bucket[: hi - lo]
-            a = T.ev()
+            if sample and b == 0:
+                a = T.ev()
             z.zero_reduce_scatter([c[lo:hi] for c in st.contrib], w, [g])
-            m = T.ev()
+            if sample and b == 0:
+                m = T.ev()
             z.zero_adam_shard_step(st.master[lo:hi], st.exp_avg[lo:hi], st.exp_avg_sq[lo:hi], st.bf16[lo:hi], g, hp)
-            e = T.ev()
-            if hi - lo == st.bucket:
+            if sample and b == 0:
                 T.span("rs", a, m)
-                T.span("adam", m, e)
-    stop = T.ev()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall0
-    ms_step = start.elapsed_time(stop) / args.steps
+                T.span("adam", m, T.ev())
+
+    def fused_step(hp, sample):
+        for b, (lo, hi) in enumerate(st.bounds):
+            if sample and b == 0:
+                a = T.ev()
+            z.zero_reduce_scatter_adam([c[lo:hi] for c in st.contrib], w, [st.master[lo:hi]], [st.exp_avg[lo:hi]],
+                                       [st.exp_avg_sq[lo:hi]], [st.bf16[lo:hi]], hp)
+            if sample and b == 0:
+                T.span("fused", a, T.ev())
+
+    def timed(step_fn):
+        nonlocal t
+        for _ in range(args.warmup):
+            t += 1
+            step_fn(wl.hparams(step=t), False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start = T.ev()
+        for i in range(args.steps):
+            t += 1
+            step_fn(wl.hparams(step=t), i % SAMPLE_EVERY == 0)
+        stop = T.ev()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps, time.perf_counter() - t0
+
+    assert st.bounds[0][1] - st.bounds[0][0] == B
+    ms_step, wall = timed(sep_step)
     step_bytes = (B_RS(n) + B_ADAM) * wl.psi
     rs_ms, adam_ms = T.ms("rs"), T.ms("adam")
-    B = st.bucket
     out = _base(wl.description, wl.psi / (ms_step * 1e-3), ms_step, args,
                 {"params": wl.psi, "n_ranks": n, "bucket": B, "buckets": len(st.bounds),
                  "step": "per bucket: reduce 4 pre-sliced contributions + owner Adam update"})
@@ -329,24 +362,12 @@ def run_owner_share(args):
         "hbm_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "wall_s_timed": wall,
         "kernels": {"reduce_scatter": {"ms": rs_ms, "bytes": B_RS(n) * B, "gbs": B_RS(n) * B / (rs_ms * 1e-3) / 1e9},
-                    "adam_shard_step": {"ms": adam_ms, "bytes": B_ADAM * B, "gbs": B_ADAM * B / (adam_ms * 1e-3) / 1e9}},
+                    "adam_shard_step": {"ms": adam_ms, "bytes": B_ADAM * B, "gbs": B_ADAM * B / (adam_ms * 1e-3) / 1e9},
+                    "timing": f"event pairs around the first bucket on every {SAMPLE_EVERY}th timed step"},
         "roofline": _roofline("adam_shard_step", wl.name, adam_ms, B),
     })
     # the same step with the fused reduce + update kernel per bucket (34 B/param)
-    torch.cuda.synchronize()
-    start = T.ev()
-    for _ in range(args.steps):
-        t += 1
-        hp = wl.hparams(step=t)
-        for b, (lo, hi) in enumerate(st.bounds):
-            a = T.ev()
-            z.zero_reduce_scatter_adam([c[lo:hi] for c in st.contrib], w, [st.master[lo:hi]], [st.exp_avg[lo:hi]],
-                                       [st.exp_avg_sq[lo:hi]], [st.bf16[lo:hi]], hp)
-            if hi - lo == st.bucket:
-                T.span("fused", a, T.ev())
-    stop = T.ev()
-    torch.cuda.synchronize()
-    f_ms = start.elapsed_time(stop) / args.steps
+    f_ms, _ = timed(fused_step)
     fk = T.ms("fused")
     out["fused_variant"] = {"ms_per_step": f_ms, "value": wl.psi / (f_ms * 1e-3),
                             "hbm_gbs_algorithmic": (2 * n + 26) * wl.psi / (f_ms * 1e-3) / 1e9,
@@ -378,53 +399,50 @@ def run_chain(args):
     w = z.zero_rank_weights(None, n)
     T = Timer()
     U = len(ch.units)
+    # The backward computation that produces each unit's N contributions is
+    # not part of the path: they are generated once, for the largest unit,
+    # before the timed region, and every unit's backward reads its prefix.
+    fill.chain_unit_grads(gen, wl, 0, ch.grads, ch.max_pad, tmp)
 
-    def step(t, timed, fused=False):
+    def step(t, mid=None, fused=False):
         hp = wl.hparams(step=t)
-        pre = "f_" if fused else ""
         for u in range(U):                      # forward: gather, use, release
-            a = T.ev() if timed else None
             ch.forward_unit(u)
-            if timed:
-                T.span(pre + "ag", a, T.ev())
+        if mid is not None:
+            mid.append(T.ev())
         for u in reversed(range(U)):            # backward
-            pad = ch.units[u][2]
-            fill.chain_unit_grads(gen, wl, u, ch.grads, pad, tmp)   # producer, not timed
-            a = T.ev() if timed else None
             if fused:
                 ch.backward_unit_fused(u, w, hp)
             else:
                 ch.backward_unit(u, w, hp)
-            if timed:
-                T.span(pre + "bwd", a, T.ev())
 
-    torch.cuda.synchronize()
     t = 0
-    for _ in range(args.warmup):
-        t += 1
-        step(t, False)
-    torch.cuda.synchronize()
-    # per-kernel durations on one representative layer unit (timed separately)
-    t_wall0 = time.perf_counter()
-    for _ in range(args.steps):
-        t += 1
-        step(t, True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall0
-    fwd_ms = T.total_ms("ag") / args.steps
-    bwd_ms = T.total_ms("bwd") / args.steps
-    ms_step = fwd_ms + bwd_ms
-    for _ in range(args.steps):
-        t += 1
-        step(t, True, fused=True)
-    torch.cuda.synchronize()
-    f_ms = (T.total_ms("f_ag") + T.total_ms("f_bwd")) / args.steps
+
+    def timed(fused):
+        nonlocal t
+        for _ in range(args.warmup):
+            t += 1
+            step(t, fused=fused)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        marks = [T.ev()]
+        for _ in range(args.steps):
+            t += 1
+            step(t, marks, fused=fused)
+            marks.append(T.ev())
+        torch.cuda.synchronize()
+        fwd = sum(marks[2 * i].elapsed_time(marks[2 * i + 1]) for i in range(args.steps)) / args.steps
+        tot = marks[0].elapsed_time(marks[-1]) / args.steps
+        return tot, fwd, time.perf_counter() - t0
+
+    ms_step, fwd_ms, wall = timed(False)
+    bwd_ms = ms_step - fwd_ms
+    f_ms, _, _ = timed(True)
     psi_pad = sum(u[2] for u in ch.units)
     step_bytes = (B_RS(n) + B_ADAM + B_AG) * psi_pad
-    # kernel-level timing of one layer unit
+    # kernel-level timing of one layer unit (not the timed region)
     lay = 1
     pad, s = ch.units[lay][2], ch.units[lay][3]
-    fill.chain_unit_grads(gen, wl, lay, ch.grads, pad, tmp)
     hp = wl.hparams(step=t + 1)
     for _ in range(3):
         a = T.ev()
@@ -444,11 +462,11 @@ def run_chain(args):
     out = _base(wl.description, wl.psi / (ms_step * 1e-3), ms_step, args,
                 {"params": wl.psi, "n_ranks": n, "units": U,
                  "step": "forward: 34 all-gathers into a released view; backward (reverse): "
-                         "reduce-scatter + 4 owner Adam updates per unit; gradient generation excluded"})
+                         "reduce-scatter + 4 owner Adam updates per unit; contributions generated before the timed region"})
     out.update({
         "hbm_gbs_algorithmic": step_bytes / (ms_step * 1e-3) / 1e9,
         "hbm_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "forward_ms": fwd_ms, "backward_ms": bwd_ms, "wall_s_timed_incl_generation": wall,
+        "forward_ms": fwd_ms, "backward_ms": bwd_ms, "wall_s_timed": wall,
         "memory": {"persistent_bytes_all_owners": persistent,
                    "ledger_zero3_bytes_all_owners": 16 * wl.psi,
                    "peak_allocated_bytes": peak},
