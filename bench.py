@@ -137,37 +137,71 @@ def _base(workload_desc, value, ms_step, args, extra_cfg=None):
 
 
 # --------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(target_s: float):
-    """The oracle, as it stands, on 2^22-parameter slices of the 7B-class layer
-    workload (reduce-scatter of 4 count-weighted BF16 ranks, AdamW, BF16 pack,
-    gather), repeated until target_s seconds of CPU work.  numpy's element-wise
-    ufuncs run on one thread."""
+CPU_SLICE = 1 << 22
+
+
+def _cpu_slice_worker(slice_index: int, target_s: float):
+    """One process: the oracle's sharded step on one 2^22-parameter slice of the
+    7B-class layer workload, repeated until target_s seconds have passed.
+    Returns (parameters stepped, seconds)."""
     import oracle
     import synthetic as S
     from synthetic.workloads import LAYER_7B as wl
 
-    n, chunk = wl.n_ranks, 1 << 22
-    grads = S.host_rank_grads(wl.seed, n, chunk, wl.grad_sigma, S.rank_scales(wl.seed, n))
-    p, m, v = S.host_state(wl.seed + 1, chunk, wl.master_sigma)
+    n, chunk = wl.n_ranks, CPU_SLICE
+    seed = wl.seed + 1000 * slice_index
+    grads = S.host_rank_grads(seed, n, chunk, wl.grad_sigma, S.rank_scales(wl.seed, n))
+    p, m, v = S.host_state(seed + 1, chunk, wl.master_sigma)
     w = oracle.weights_from_counts(wl.extra["token_counts"])
     sc = oracle.adam_scalars(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay, 1)
     s = chunk // n
-    done, reps = 0, 0
+    done = 0
     t0 = time.perf_counter()
     while True:
         oracle.sharded_step(grads, w, [p[k * s:(k + 1) * s] for k in range(n)],
                             [m[k * s:(k + 1) * s] for k in range(n)],
                             [v[k * s:(k + 1) * s] for k in range(n)], sc)
         done += chunk
-        reps += 1
         el = time.perf_counter() - t0
         if el >= target_s:
-            break
-    return {"value": done / el, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": (f"oracle sharded step on a 2^22-param slice of the 7B-class layer "
-                       f"(4 count-weighted BF16 ranks, AdamW, BF16 pack, all-gather), "
-                       f"{reps} repetitions in {el:.1f} s on 1 thread (numpy ufuncs); "
-                       f"host has {os.cpu_count()} CPUs")}
+            return done, el
+
+
+def cpu_baseline(target_s: float):
+    """The oracle, as it stands, on 2^22-parameter slices of the 7B-class layer
+    workload (reduce-scatter of 4 count-weighted BF16 ranks, AdamW, BF16 pack,
+    gather): first in this process on one thread for target_s seconds, then
+    in one process per available core (at most 16), each on its own slice,
+    for target_s seconds.  The slices are independent, as the shards are.
+    Runs before the GPU is touched."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import platform
+
+    done1, el1 = _cpu_slice_worker(0, target_s)
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    with cf.ProcessPoolExecutor(cores, mp_context=mp.get_context("spawn")) as ex:
+        # one warm-up task per worker so that interpreter and import time stay out
+        list(ex.map(_cpu_slice_worker, range(cores), [0.0] * cores))
+        res = list(ex.map(_cpu_slice_worker, range(cores), [target_s] * cores))
+    done_all = sum(r[0] for r in res)
+    wall = max(r[1] for r in res)      # the workers' step loops run concurrently
+    model = platform.processor() or platform.machine()
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": done_all / wall, "unit": "params/s", "cores": cores, "kind": "oracle",
+            "sample": (f"oracle sharded step (4 count-weighted BF16 ranks, AdamW, BF16 pack, all-gather) "
+                       f"on 2^22-param slices of the 7B-class layer: {cores} processes, one slice each, "
+                       f"{done_all // CPU_SLICE} slice-steps, the slowest process's loop {wall:.1f} s; numpy ufuncs, one thread "
+                       f"per process; {model}, {os.cpu_count()} CPUs visible, {cores} in the affinity mask "
+                       f"used (capped at 16)"),
+            "single_thread": {"value": done1 / el1, "unit": "params/s", "cores": 1,
+                              "sample": f"{done1 // CPU_SLICE} slice-steps in {el1:.1f} s on one thread"}}
 
 
 # --------------------------------------------------------------------------- flat units
@@ -399,6 +433,7 @@ def run_chain(args):
     w = z.zero_rank_weights(None, n)
     T = Timer()
     U = len(ch.units)
+    rg = bool(args.regather_bwd)
     # The backward computation that produces each unit's N contributions is
     # not part of the path: they are generated once, for the largest unit,
     # before the timed region, and every unit's backward reads its prefix.
@@ -412,9 +447,9 @@ def run_chain(args):
             mid.append(T.ev())
         for u in reversed(range(U)):            # backward
             if fused:
-                ch.backward_unit_fused(u, w, hp)
+                ch.backward_unit_fused(u, w, hp, regather=rg)
             else:
-                ch.backward_unit(u, w, hp)
+                ch.backward_unit(u, w, hp, regather=rg)
 
     t = 0
 
@@ -439,7 +474,7 @@ def run_chain(args):
     bwd_ms = ms_step - fwd_ms
     f_ms, _, _ = timed(True)
     psi_pad = sum(u[2] for u in ch.units)
-    step_bytes = (B_RS(n) + B_ADAM + B_AG) * psi_pad
+    step_bytes = (B_RS(n) + B_ADAM + B_AG * (2 if rg else 1)) * psi_pad
     # kernel-level timing of one layer unit (not the timed region)
     lay = 1
     pad, s = ch.units[lay][2], ch.units[lay][3]
@@ -460,9 +495,11 @@ def run_chain(args):
     adam_ms = T.ms("k_adam")
     persistent = sum(x.numel() * x.element_size() for x in ch.master + ch.exp_avg + ch.exp_avg_sq + ch.bf16)
     out = _base(wl.description, wl.psi / (ms_step * 1e-3), ms_step, args,
-                {"params": wl.psi, "n_ranks": n, "units": U,
+                {"params": wl.psi, "n_ranks": n, "units": U, "regather_bwd": rg,
                  "step": "forward: 34 all-gathers into a released view; backward (reverse): "
-                         "reduce-scatter + 4 owner Adam updates per unit; contributions generated before the timed region"})
+                         + ("all-gather again, " if rg else "")
+                         + "reduce-scatter + 4 owner Adam updates per unit; contributions generated "
+                           "before the timed region"})
     out.update({
         "hbm_gbs_algorithmic": step_bytes / (ms_step * 1e-3) / 1e9,
         "hbm_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
@@ -475,7 +512,8 @@ def run_chain(args):
                                               "gbs": B_ADAM * s / (adam_ms * 1e-3) / 1e9}},
         "roofline": _roofline("adam_shard_step", wl.name, adam_ms, s),
         "fused_variant": {"ms_per_step": f_ms, "value": wl.psi / (f_ms * 1e-3),
-                          "hbm_gbs_algorithmic": (2 * n + 26 + B_AG) * psi_pad / (f_ms * 1e-3) / 1e9},
+                          "hbm_gbs_algorithmic": (2 * n + 26 + B_AG * (2 if rg else 1)) * psi_pad
+                          / (f_ms * 1e-3) / 1e9},
     })
     out["copy_ceiling_gbs_same_run"] = copy_ceiling_gbs()
     return out
@@ -630,11 +668,16 @@ def main():
     ap.add_argument("--workload", default="layer7b_weighted_adamw", choices=sorted(RUNNERS))
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--regather-bwd", action="store_true",
+                    help="zero3_chain_llama8b: gather each unit again before its backward reduce")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the ranks are "
               "simulated as buffers in one GPU's HBM and no multi-GPU path is built.", file=sys.stderr)
         sys.exit(2)
+    cpu = None
+    if args.workload == "layer7b_weighted_adamw" and not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_baseline_seconds)    # before anything touches the GPU
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -645,8 +688,8 @@ def main():
         import __graft_entry__
         __graft_entry__.build()
     out = RUNNERS[args.workload](args)
-    if args.workload == "layer7b_weighted_adamw" and not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.cpu_baseline_seconds)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

@@ -149,3 +149,45 @@ def test_chain_backward_fused_equals_separate():
         assert torch.equal(xa.view(torch.int32), xb.view(torch.int32))
     for xa, xb in zip(a.bf16, b.bf16):
         assert torch.equal(xa.view(torch.int16), xb.view(torch.int16))
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_chain_backward_regather(fused):
+    # backward gathers each unit again before its reduce (essay, ZeRO-3 的一次完整计算):
+    # the regathered view equals that step's forward view, and the state
+    # equals the chain without the regather, bit for bit
+    from zero_sharded_optimizer_reduce_amd.drivers import Zero3Chain
+    units = [("emb", [("e", 4 * 256 * 5)]), ("layer", [("a", 4000), ("b", 1000)]), ("head", [("h", 4 * 256 * 2)])]
+    n = 4
+    gen = S.DeviceGen(321)
+    chains = [Zero3Chain(units, n), Zero3Chain(units, n)]
+    for ch in chains:
+        for k in range(n):
+            gen.normal_(ch.master[k], 0.02, 1, k)
+            ch.bf16[k].copy_(ch.master[k])
+    w = z.zero_rank_weights(None, n)
+    tmp = torch.empty(chains[0].max_pad, device="cuda")
+    for t in (1, 2):
+        hp = _hp(0.0, t)
+        fwd = {}
+        for u in range(len(units)):
+            for ch in chains:
+                v = ch.forward_unit(u)
+            fwd[u] = v.clone()
+        for u in reversed(range(len(units))):
+            pad = chains[0].units[u][2]
+            for ch in chains:
+                for r, g in enumerate(ch.grads):
+                    gen.bf16_normal_(g[:pad], 1e-3, 70 + t, u, r, tmp=tmp[:pad])
+            step = (lambda ch, **kw: ch.backward_unit_fused(u, w, hp, **kw)) if fused else \
+                (lambda ch, **kw: ch.backward_unit(u, w, hp, **kw))
+            step(chains[0])
+            step(chains[1], regather=True)
+            # the regathered view was written before this unit's update
+            assert torch.equal(chains[1].view[:pad].view(torch.int16), fwd[u].view(torch.int16)), (t, u)
+    torch.cuda.synchronize()
+    a, b = chains
+    for xa, xb in zip(a.master + a.exp_avg + a.exp_avg_sq, b.master + b.exp_avg + b.exp_avg_sq):
+        assert torch.equal(xa.view(torch.int32), xb.view(torch.int32))
+    for xa, xb in zip(a.bf16, b.bf16):
+        assert torch.equal(xa.view(torch.int16), xb.view(torch.int16))

@@ -144,17 +144,26 @@ class Zero3Chain:
         zero_all_gather_layer(self.owner_slices(u, self.bf16), view, stream=stream)
         return view
 
-    def backward_unit_fused(self, u: int, weights, hp, stream=None):
+    def backward_unit_fused(self, u: int, weights, hp, stream=None, regather: bool = False):
         """backward_unit with the fused reduce-scatter + update kernel (one
-        launch for the 4 owners; the reduced shards are not stored)."""
+        launch per owner; the reduced shards are not stored)."""
         pad = self.units[u][2]
+        if regather:
+            self.forward_unit(u, stream=stream)
         zero_reduce_scatter_adam([g[:pad] for g in self.grads], weights,
                                  *(self.owner_slices(u, x) for x in
                                    (self.master, self.exp_avg, self.exp_avg_sq, self.bf16)),
                                  hp, stream=stream)
 
-    def backward_unit(self, u: int, weights, hp, stream=None):
+    def backward_unit(self, u: int, weights, hp, stream=None, regather: bool = False):
+        """Reduce-scatter unit u's N contributions into the owners' FP32
+        gradient shards, then each owner's update.  With regather, the unit's
+        weights are first gathered again into the view, as the backward pass
+        needs them (essay, ZeRO-3 的一次完整计算: backward gathers each layer
+        again before computing its gradient)."""
         pad, s = self.units[u][2], self.units[u][3]
+        if regather:
+            self.forward_unit(u, stream=stream)
         zero_reduce_scatter([g[:pad] for g in self.grads], weights,
                             [g[:s] for g in self.grad_shards], stream=stream)
         for k, (p, m, v, b) in enumerate(zip(*(self.owner_slices(u, x) for x in
