@@ -512,8 +512,9 @@ constexpr int kGatherBlock = 64;
 constexpr unsigned kAdamResidencyLds = 13 * 1024;    // 160 / 13 -> 12 workgroups
 constexpr unsigned kFusedResidencyLds = 16 * 1024;   // 160 / 16 -> 10 workgroups
 
-// Vectors per lane per loop iteration (measured: 1 is best with full grids).
-constexpr int kRsU = 2;
+// Vectors per lane per loop iteration (measured: 1 is best with full grids;
+// for the reduce, 2 and 4 were 1-3% slower on the layer shard and a 64M bucket).
+constexpr int kRsU = 1;
 constexpr int kFusedU = 1;
 constexpr int kAdamU = 1;
 constexpr int kGatherU = 1;
