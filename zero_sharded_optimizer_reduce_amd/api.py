@@ -32,6 +32,8 @@ def _dev(t: torch.Tensor, what: str, dtypes) -> int:
         raise TypeError(f"{what}: expected a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{what}: must be a device tensor, got {t.device}")
+    if t.device.index is not None and t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{what}: on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
     if t.dtype not in dtypes:
         raise TypeError(f"{what}: dtype {t.dtype} not in {dtypes}")
     if not t.is_contiguous():
