@@ -310,8 +310,70 @@ def run_flat(args, wl, numels, grad_scales=None, counts=None):
                          "gbs": (2 * n + 26) * pad / (fk * 1e-3) / 1e9},
         "hbm_gbs_algorithmic": (2 * n + 26 + B_AG) * pad / (f_ms * 1e-3) / 1e9,
     }
+    out["next_rows"] = _next_rows(args, st, grads, w, wl, timed, T)
     out["copy_ceiling_gbs_same_run"] = copy_ceiling_gbs()
     return out
+
+
+def _next_rows(args, st, grads, w, wl, timed, T):
+    """The optional rows beyond the sharded step, each timed on the same
+    buffers: the step with a global gradient-norm clip, the reduce with FP32
+    contributions, and the reduce in accumulate mode."""
+    import torch
+
+    import zero_sharded_optimizer_reduce_amd as z
+    from zero_sharded_optimizer_reduce_amd import _lib
+
+    n, pad = st.n, st.psi_pad
+    ws = torch.empty(n * _lib.ZERO_NORM_BLOCKS, dtype=torch.float64, device="cuda")
+    norm_sq = torch.empty(1, dtype=torch.float64, device="cuda")
+    coef = torch.empty(1, dtype=torch.float32, device="cuda")
+
+    def clipped_step(hp, sample):
+        st.reduce_scatter(grads, w)
+        a = T.ev() if sample else None
+        z.zero_grad_norm_sq(st.grad, ws, norm_sq, max_norm=1.0, clip_coef_out=coef)
+        if sample:
+            T.span("norm", a, T.ev())
+        for k in range(n):
+            z.zero_adam_shard_step_scaled(st.master[k], st.exp_avg[k], st.exp_avg_sq[k], st.bf16[k], st.grad[k],
+                                          coef, hp)
+        st.all_gather()
+
+    c_ms, _ = timed(clipped_step, "norm")
+    norm_ms = T.ms("norm")
+    res = {"grad_norm_clip": {
+        "ms_per_step": c_ms, "value": st.psi / (c_ms * 1e-3),
+        "step": "reduce-scatter + global gradient norm (FP64, fixed order) and clip coefficient (max_norm 1.0) "
+                "+ 4 owner updates on the scaled gradient + all-gather, 50 B/param",
+        "hbm_gbs_algorithmic": 50 * pad / (c_ms * 1e-3) / 1e9,
+        "norm_kernels": {"ms": norm_ms, "bytes": 4 * pad, "gbs": 4 * pad / (norm_ms * 1e-3) / 1e9,
+                         "timing": f"event pair around the norm call on every {SAMPLE_EVERY}th timed step"}}}
+
+    def run_calls(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a = T.ev()
+        for _ in range(reps):
+            fn()
+        b = T.ev()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    reps = max(4, args.steps // 4)
+    acc_ms = run_calls(lambda: z.zero_reduce_scatter(grads, w, st.grad, accumulate=True), reps)
+    res["reduce_scatter_accumulate"] = {
+        "ms": acc_ms, "bytes": B_RS_ACC(n) * pad, "gbs": B_RS_ACC(n) * pad / (acc_ms * 1e-3) / 1e9,
+        "what": "shard += reduction of the 4 BF16 contributions (micro-batch accumulation), 4 owner launches"}
+    g32 = [g.float() for g in grads]
+    f_ms = run_calls(lambda: z.zero_reduce_scatter_f32(g32, w, st.grad), reps)
+    res["reduce_scatter_f32"] = {
+        "ms": f_ms, "bytes": (4 * n + 4) * pad, "gbs": (4 * n + 4) * pad / (f_ms * 1e-3) / 1e9,
+        "what": "reduce-scatter of 4 FP32 contributions (gradients kept in FP32), 4 owner launches"}
+    del g32, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_layer7b(args):

@@ -94,16 +94,16 @@ __device__ __forceinline__ f32x4 reduce4(const f32x4 (&x)[NMAX], int n, const fl
 }
 
 // FP32 contributions (gradients stored in FP32): 16-byte load per rank.
-template <int N, bool ACC>
-__global__ __launch_bounds__(kBlock) void rs_f32_vec_kernel(RsParams p) {
+template <int N, bool ACC, int BS>
+__global__ __launch_bounds__(BS) void rs_f32_vec_kernel(RsParams p) {
   constexpr int NMAX = N > 0 ? N : ZERO_MAX_RANKS;
   const int n = N > 0 ? N : p.n_ranks;
   const int k = blockIdx.y;
   const int64_t nvec = p.shard >> 2;
   const int64_t off = static_cast<int64_t>(k) * nvec;
   f32x4* __restrict__ out = reinterpret_cast<f32x4*>(p.out[k]);
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nvec;
-       i += static_cast<int64_t>(gridDim.x) * kBlock) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * BS + threadIdx.x; i < nvec;
+       i += static_cast<int64_t>(gridDim.x) * BS) {
     f32x4 x[NMAX];
 #pragma unroll
     for (int r = 0; r < NMAX; ++r)
@@ -481,7 +481,7 @@ int device_cus() {
 }
 
 // Blocks along x for `units` work items per owner, each block covering
-// kBlock*u of them per loop iteration.
+// bs*u of them per loop iteration.
 unsigned grid_x(int64_t units, int u, int n_y, int bs = kBlock) {
   const int64_t per_iter = static_cast<int64_t>(bs) * u;
   int64_t need = (units + per_iter - 1) / per_iter;
@@ -506,11 +506,18 @@ constexpr int kGatherBlock = 64;
 // update (8 streams), 10 for the fused kernel (11 streams).  With fewer
 // requests in flight the HBM keeps more row hits: measured on MI355X, the
 // update goes from 6.1-6.2 to 6.5-6.6 TB/s, the fused kernel from 5.8-6.0 to
-// 6.55 TB/s.  The reduce (5 streams) and the gather (2) are fastest without a
-// cap.  The byte counts are multiples of 1 KiB and give the same count under
+// 6.55 TB/s.  The plain reduce (5 streams) and the gather (2) are fastest
+// without a cap.  The byte counts are multiples of 1 KiB and give the same count under
 // any allocation granularity up to 1 KiB.
 constexpr unsigned kAdamResidencyLds = 13 * 1024;    // 160 / 13 -> 12 workgroups
 constexpr unsigned kFusedResidencyLds = 16 * 1024;   // 160 / 16 -> 10 workgroups
+// The reduce in accumulate mode (6 streams) and with FP32 contributions
+// (5 streams of 16-byte loads) are fastest with 64-lane workgroups capped at
+// 20 and 16 per CU: 6.14 -> 6.4 and 6.1 -> 6.4 TB/s on the 7B-layer shards.
+constexpr int kRsAccBlock = 64;
+constexpr unsigned kRsAccResidencyLds = 8 * 1024;    // 160 / 8 -> 20 workgroups
+constexpr int kRsF32Block = 64;
+constexpr unsigned kRsF32ResidencyLds = 10 * 1024;   // 160 / 10 -> 16 workgroups
 
 // Vectors per lane per loop iteration (measured: 1 is best with full grids;
 // for the reduce, 2 and 4 were 1-3% slower on the layer shard and a 64M bucket).
@@ -534,8 +541,9 @@ template <int N, bool ACC>
 hipError_t rs_vec_launch(const RsParams& p, int n_shards, hipStream_t s) {
   for (int k = 0; k < n_shards; ++k) {
     const RsParams q = owner_slice(p, k, p.shard);
-    dim3 grid(grid_x(p.shard >> 2, kRsU, 1, kRsBlock), 1);
-    hipLaunchKernelGGL((rs_vec_kernel<N, ACC, kRsU, kRsBlock>), grid, dim3(kRsBlock), 0, s, q);
+    constexpr int bs = ACC ? kRsAccBlock : kRsBlock;
+    dim3 grid(grid_x(p.shard >> 2, kRsU, 1, bs), 1);
+    hipLaunchKernelGGL((rs_vec_kernel<N, ACC, kRsU, bs>), grid, dim3(bs), ACC ? kRsAccResidencyLds : 0u, s, q);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -570,8 +578,8 @@ template <int N, bool ACC>
 hipError_t rs_f32_vec_launch(const RsParams& p, int n_shards, hipStream_t s) {
   for (int k = 0; k < n_shards; ++k) {
     const RsParams q = owner_slice(p, k, 2 * p.shard);   // FP32 elements = 2 BF16 units
-    dim3 grid(grid_x(p.shard >> 2, 1, 1), 1);
-    hipLaunchKernelGGL((rs_f32_vec_kernel<N, ACC>), grid, dim3(kBlock), 0, s, q);
+    dim3 grid(grid_x(p.shard >> 2, 1, 1, kRsF32Block), 1);
+    hipLaunchKernelGGL((rs_f32_vec_kernel<N, ACC, kRsF32Block>), grid, dim3(kRsF32Block), kRsF32ResidencyLds, s, q);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
