@@ -38,6 +38,21 @@ MUTATIONS = {
     "norm_not_squared": ("total += float(np.sum(x64 * x64))", "total += float(np.sum(np.abs(x64)))"),
     "clip_uses_norm_sq": ("c = float(np.float32(max_norm)) / (math.sqrt(norm_sq) + 1e-6)",
                           "c = float(np.float32(max_norm)) / (norm_sq + 1e-6)"),
+    "reversed_rank_order": ("        a = _chk32(weights[0] * _contribution_f32(rank_grads[0]))\n"
+                            "        for r in range(1, len(rank_grads)):",
+                            "        a = _chk32(weights[-1] * _contribution_f32(rank_grads[-1]))\n"
+                            "        for r in range(len(rank_grads) - 2, -1, -1):"),
+    "owner_shard_reversed_rank_order": ("    for r, g in enumerate(rank_grads):\n        term = _chk32(weights[r] * _contribution_f32(g[lo:hi]))",
+                                        "    for r, g in reversed(list(enumerate(rank_grads))):\n"
+                                        "        term = _chk32(weights[r] * _contribution_f32(g[lo:hi]))"),
+    "decay_not_scaled_by_lr": ('u = _chk32(u + _chk32(sc["weight_decay"] * p))',
+                               'u = _chk32(u + _chk32(_chk32(sc["weight_decay"] / sc["lr"]) * p))'),
+    "coupled_l2_decay": ("def _adam_step(p, m, v, g, sc):\n    m1 =",
+                         "def _adam_step(p, m, v, g, sc):\n"
+                         "    g = _chk32(g + _chk32(sc[\"weight_decay\"] * p)) if sc[\"weight_decay\"] != F32(0) else g\n"
+                         "    m1 ="),
+    "bf16_packed_from_old_master": ("return p1, m1, v1, f32_to_bf16_rne(p1)", "return p1, m1, v1, f32_to_bf16_rne(p)"),
+    "mean_weight_off": ("[float(1) / float(n_ranks)]", "[float(1) / float(n_ranks + 1)]"),
     "accumulate_mode_drops_acc": ("return _chk32(acc + reduce_full(rank_grads, weights))",
                                   "return _chk32(reduce_full(rank_grads, weights))"),
 }

@@ -30,9 +30,10 @@ def _stream(stream) -> int:
 def _dev(t: torch.Tensor, what: str, dtypes) -> int:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{what}: expected a torch.Tensor")
-    if t.device.type != "cuda":
+    d = t.get_device() if t.is_cuda else -1
+    if d < 0:
         raise ValueError(f"{what}: must be a device tensor, got {t.device}")
-    if t.device.index is not None and t.device.index != torch.cuda.current_device():
+    if d != torch.cuda.current_device():
         raise ValueError(f"{what}: on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
     if t.dtype not in dtypes:
         raise TypeError(f"{what}: dtype {t.dtype} not in {dtypes}")
