@@ -10,6 +10,8 @@
   the benchmark times: the reduced gradient of step 1 is compared in full;
   state and views on sampled windows (shard starts and ends, shard boundaries
   and random positions) at every step.
+* The same layer with the global gradient-norm clip, at full size: the FP64
+  norm against the oracle's, the clip coefficient, and the scaled update.
 """
 import numpy as np
 import pytest
@@ -137,3 +139,58 @@ def test_resume_from_saved_state_is_bit_exact():
     for xa, xc in zip(a.master + a.exp_avg + a.exp_avg_sq, c.master + c.exp_avg + c.exp_avg_sq):
         assert np.array_equal(f32_to_host(xa).view(np.uint32), f32_to_host(xc).view(np.uint32))
     assert np.array_equal(bf16_to_host(a.view), bf16_to_host(c.view))
+
+
+def test_layer7b_clipped_step():
+    # the step with the global-norm clip at the full 7B-class layer size, in the
+    # launch configuration the benchmark times: the norm against the oracle's
+    # FP64 sum (different summation order: relative 1e-12), the coefficient
+    # within 1 ulp, and the scaled update bit-exact on windows given the
+    # device's coefficient (both sides then take the same clip decision)
+    from zero_sharded_optimizer_reduce_amd import _lib
+    wl = S.WORKLOADS["layer7b_weighted_adamw"]
+    n, psi = wl.n_ranks, wl.psi
+    st = ShardedStep(S.unit_numels(S.workloads.layer_7b_tensors()), n)
+    gen = S.DeviceGen(wl.seed + 40)
+    master0 = gen.normal_(torch.empty(psi, device="cuda"), wl.master_sigma, 0)
+    st.load_master(master0)
+    w = z.zero_rank_weights(wl.extra["token_counts"], n)
+    scales = S.rank_scales(wl.seed, n)
+    grads = [torch.empty(psi, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    tmp = torch.empty(psi, dtype=torch.float32, device="cuda")
+    for r in range(n):
+        gen.bf16_normal_(grads[r], wl.grad_sigma, 1, r, scale=scales[r], tmp=tmp)
+    del tmp
+    ws = torch.empty(n * _lib.ZERO_NORM_BLOCKS, dtype=torch.float64, device="cuda")
+    norm_sq = torch.empty(1, dtype=torch.float64, device="cuda")
+    coef = torch.empty(1, dtype=torch.float32, device="cuda")
+    hp = wl.hparams(step=1)
+    max_norm = 1.0
+    print("layer7b clipped step", flush=True)
+    st.reduce_scatter(grads, w)
+    z.zero_grad_norm_sq(st.grad, ws, norm_sq, max_norm=max_norm, clip_coef_out=coef)
+    for k in range(n):
+        z.zero_adam_shard_step_scaled(st.master[k], st.exp_avg[k], st.exp_avg_sq[k], st.bf16[k], st.grad[k],
+                                      coef, hp)
+    st.all_gather()
+    torch.cuda.synchronize()
+    host_g = [bf16_to_host(g) for g in grads]
+    red = oracle.reduce_full(host_g, w)
+    ref_nsq = oracle.grad_norm_sq([red])
+    got_nsq = float(norm_sq.item())
+    assert abs(got_nsq - ref_nsq) <= 1e-12 * ref_nsq, (got_nsq, ref_nsq)
+    ref_c = oracle.clip_coefficient(ref_nsq, max_norm)
+    got_c = np.float32(coef.item())
+    assert ref_c < 1 and abs(int(got_c.view(np.int32)) - int(ref_c.view(np.int32))) <= 1, (got_c, ref_c)
+    gp = np.concatenate([f32_to_host(x) for x in st.master])
+    gm = np.concatenate([f32_to_host(x) for x in st.exp_avg])
+    gv = np.concatenate([f32_to_host(x) for x in st.exp_avg_sq])
+    gb = bf16_to_host(st.view)
+    sc = _sc(hp)
+    width = 4096
+    for a in _windows(psi, n, st.shard, np.random.default_rng(wl.seed + 40)):
+        g_ref = oracle.scale_grad(red[a:a + width], got_c)
+        z0 = np.zeros(width, np.float32)
+        ref = oracle.adam_step(f32_to_host(master0[a:a + width]), z0, z0.copy(), g_ref, sc)
+        assert_state_close(gp[a:a + width], gm[a:a + width], gv[a:a + width], gb[a:a + width], ref,
+                           f"clipped window {a}")
