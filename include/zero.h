@@ -156,8 +156,10 @@ int zero_adam_shard_step(float* master, float* exp_avg, float* exp_avg_sq, uint1
 /* zero_adam_shard_step with the gradient first multiplied by a device scalar:
  * g = g * (*grad_scale) (one binary32 multiply), then the same update.  Used
  * with the clip coefficient of zero_grad_norm_sq, which stays on the device.
- *   grad_scale   device pointer to one float (4-byte aligned), read once.
- * Errors: as zero_adam_shard_step; ZERO_ERR_ARG for a NULL grad_scale. */
+ *   grad_scale   device pointer to one float (4-byte aligned), read once; it
+ *                may not lie inside master, exp_avg, exp_avg_sq or bf16_out.
+ * Errors: as zero_adam_shard_step; ZERO_ERR_ARG for a NULL grad_scale or one
+ * inside a buffer the update writes. */
 int zero_adam_shard_step_scaled(float* master, float* exp_avg, float* exp_avg_sq,
                                 uint16_t* bf16_out, const float* grad, const float* grad_scale,
                                 int64_t n, const zero_adam_hparams* hp, void* stream);

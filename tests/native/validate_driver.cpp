@@ -53,6 +53,15 @@ int main() {
   bad = hp;
   bad.beta2 = 1.0f;
   EXPECT(check_adam(p, m, v, b, gr, 16, &bad, e) == ZERO_ERR_ARG);
+  // the device scale of the clipped update
+  const float* gs = (const float*)P(0x600000);
+  EXPECT(check_adam_scale(gs, p, m, v, b, 4096, e) == ZERO_OK);
+  EXPECT(check_adam_scale(nullptr, p, m, v, b, 4096, e) == ZERO_ERR_ARG);
+  EXPECT(check_adam_scale((const float*)P(0x600002), p, m, v, b, 4096, e) == ZERO_ERR_ALIGN);
+  EXPECT(check_adam_scale(p + 4095, p, m, v, b, 4096, e) == ZERO_ERR_ARG);       // last master element
+  EXPECT(check_adam_scale((const float*)(b + 2046), p, m, v, b, 4096, e) == ZERO_ERR_ARG);  // inside bf16_out
+  EXPECT(check_adam_scale(p + 4096, p, m, v, b, 4096, e) == ZERO_OK);            // just past master
+  EXPECT(check_adam_scale(gr, p, m, v, b, 4096, e) == ZERO_OK);                  // inside the read-only gradient
   // scalars
   zero_adam_scalars sc;
   EXPECT(adam_scalars(&hp, &sc, e) == ZERO_OK);

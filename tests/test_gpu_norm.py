@@ -88,3 +88,18 @@ def test_norm_validation():
         z.zero_grad_norm_sq(x, torch.empty(10, dtype=torch.float64, device="cuda"), out)
     with pytest.raises(z.ZeroError):           # clip requested without a positive max_norm
         z.zero_grad_norm_sq(x, _ws(1), out, max_norm=0.0, clip_coef_out=torch.empty(1, device="cuda"))
+
+
+def test_scaled_update_rejects_a_scale_inside_its_outputs():
+    n = 1024
+    p, m, v, g = (torch.zeros(n, device="cuda") for _ in range(4))
+    b = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, step=1)
+    with pytest.raises(z.ZeroError, match="ZERO_ERR_ARG"):
+        z.zero_adam_shard_step_scaled(p, m, v, b, g, p[5:6], hp)      # the scale is a master element
+    with pytest.raises(z.ZeroError, match="ZERO_ERR_ARG"):
+        z.zero_adam_shard_step_scaled(p, m, v, b, g, v[-1:], hp)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(p) == 0 and torch.count_nonzero(m) == 0   # nothing was launched
+    z.zero_adam_shard_step_scaled(p, m, v, b, g, g[:1], hp)             # inside the read-only gradient: fine
+    torch.cuda.synchronize()

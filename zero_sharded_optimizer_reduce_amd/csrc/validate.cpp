@@ -214,6 +214,21 @@ int check_adam(const float* master, const float* exp_avg, const float* exp_avg_s
   return ZERO_OK;
 }
 
+int check_adam_scale(const float* grad_scale, const float* master, const float* exp_avg,
+                     const float* exp_avg_sq, const uint16_t* bf16_out, int64_t n, Err& e) {
+  if (!grad_scale) return set_err(e, ZERO_ERR_ARG, "adam: NULL grad_scale");
+  if (reinterpret_cast<uintptr_t>(grad_scale) & 3u)
+    return set_err(e, ZERO_ERR_ALIGN, "adam: grad_scale not 4-byte aligned");
+  // every workgroup reads the scale while others write the state: it must not
+  // lie inside a buffer the update writes
+  const Range sc = range_of(grad_scale, 4);
+  const Range outs[4] = {range_of(master, n * 4), range_of(exp_avg, n * 4), range_of(exp_avg_sq, n * 4),
+                         range_of(bf16_out, n * 2)};
+  for (const Range& r : outs)
+    if (overlaps(sc, r)) return set_err(e, ZERO_ERR_ARG, "adam: grad_scale overlaps a buffer the update writes");
+  return ZERO_OK;
+}
+
 int check_all_gather(const void* const* shards, int n_shards, int64_t shard_bytes,
                      const void* full_view, Err& e) {
   if (!shards) return set_err(e, ZERO_ERR_ARG, "all_gather: NULL shard table");

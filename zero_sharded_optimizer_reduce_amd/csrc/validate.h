@@ -34,6 +34,10 @@ int check_adam(const float* master, const float* exp_avg, const float* exp_avg_s
                const uint16_t* bf16_out, const float* grad, int64_t n,
                const zero_adam_hparams* hp, Err& e);
 
+// The device scale of zero_adam_shard_step_scaled: non-NULL, 4-byte aligned,
+// outside every buffer the update writes.
+int check_adam_scale(const float* grad_scale, const float* master, const float* exp_avg,
+                     const float* exp_avg_sq, const uint16_t* bf16_out, int64_t n, Err& e);
 int check_all_gather(const void* const* shards, int n_shards, int64_t shard_bytes,
                      const void* full_view, Err& e);
 

@@ -103,8 +103,10 @@ static int adam_common(float* master, float* exp_avg, float* exp_avg_sq, uint16_
   int st = check_adam(master, exp_avg, exp_avg_sq, bf16_out, grad, n, hp, e);
   if (st) return fail(st, e.msg);
   if (n == 0) return ZERO_OK;
-  if (grad_scale && (reinterpret_cast<uintptr_t>(grad_scale) & 3u))
-    return fail(ZERO_ERR_ALIGN, "adam: grad_scale not 4-byte aligned");
+  if (grad_scale) {
+    st = check_adam_scale(grad_scale, master, exp_avg, exp_avg_sq, bf16_out, n, e);
+    if (st) return fail(st, e.msg);
+  }
   AdamParams a;
   memset(&a, 0, sizeof a);
   a.p = master;
