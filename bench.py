@@ -310,6 +310,26 @@ def run_flat(args, wl, numels, grad_scales=None, counts=None):
                          "gbs": (2 * n + 26) * pad / (fk * 1e-3) / 1e9},
         "hbm_gbs_algorithmic": (2 * n + 26 + B_AG) * pad / (f_ms * 1e-3) / 1e9,
     }
+
+    # the same fused step, also storing the reduced FP32 shards: every output of
+    # the separate-kernel step, 42 B/param
+    def fused_gout_step(hp, sample):
+        a = T.ev() if sample else None
+        z.zero_reduce_scatter_adam(grads, w, st.master, st.exp_avg, st.exp_avg_sq, st.bf16, hp, grad_out=st.grad)
+        if sample:
+            T.span(sample, a, T.ev())
+        st.all_gather()
+
+    fg_ms, _ = timed(fused_gout_step, "fused4g")
+    fgk = T.ms("fused4g")
+    out["fused_variant_storing_grad"] = {
+        "ms_per_step": fg_ms, "value": st.psi / (fg_ms * 1e-3),
+        "step": "fused reduce-scatter + owner updates that also store the reduced FP32 shards + all-gather, "
+                "42 B/param (the same outputs as the separate kernels)",
+        "fused_kernel": {"ms": fgk / n, "bytes": (2 * n + 30) * st.shard,
+                         "gbs": (2 * n + 30) * pad / (fgk * 1e-3) / 1e9},
+        "hbm_gbs_algorithmic": (2 * n + 30 + B_AG) * pad / (fg_ms * 1e-3) / 1e9,
+    }
     out["next_rows"] = _next_rows(args, st, grads, w, wl, timed, T)
     out["copy_ceiling_gbs_same_run"] = copy_ceiling_gbs()
     return out
