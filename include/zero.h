@@ -208,6 +208,36 @@ int zero_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* ran
                              uint16_t* const* bf16_out, const float* const* grad_acc,
                              float* const* grad_out, const zero_adam_hparams* hp, void* stream);
 
+/* Graph-capturable forms of the owner update and of the fused call: the same
+ * arithmetic, with the step's scalars read from device memory when the kernel
+ * runs instead of being passed by value at the call.  A caller that captures
+ * a step into a HIP graph writes each step's scalars (zero_adam_scalars_compute
+ * on the host, then a copy to the device struct on the replay stream) before
+ * each replay; the captured launches then apply that step's bias corrections.
+ * The decay term is applied when the device struct's weight_decay is non-zero,
+ * exactly as the host-scalar forms decide it, so results are bit-identical to
+ * zero_adam_shard_step / zero_adam_shard_step_scaled / zero_reduce_scatter_adam
+ * with the hyper-parameters the scalars were computed from.  Rank weights are
+ * still passed by value (a captured graph keeps the weights of the capture).
+ *
+ *   scalars_dev  device pointer to one zero_adam_scalars (4-byte aligned),
+ *                filled by the caller from zero_adam_scalars_compute; it may
+ *                not overlap a buffer the call writes.  Its values are not
+ *                validated (they were, when computed).
+ *   grad_scale   (zero_adam_shard_step_dev) NULL, or a device float the
+ *                gradient is multiplied by, as in zero_adam_shard_step_scaled.
+ * Errors: as the host-scalar forms, without the hyper-parameter checks, plus
+ * ZERO_ERR_ARG / ZERO_ERR_ALIGN for scalars_dev. */
+int zero_adam_shard_step_dev(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* bf16_out,
+                             const float* grad, const float* grad_scale, int64_t n,
+                             const zero_adam_scalars* scalars_dev, void* stream);
+int zero_reduce_scatter_adam_dev(const uint16_t* const* rank_grads, const float* rank_weights,
+                                 int n_ranks, int64_t numel, int n_shards, float* const* master,
+                                 float* const* exp_avg, float* const* exp_avg_sq,
+                                 uint16_t* const* bf16_out, const float* const* grad_acc,
+                                 float* const* grad_out, const zero_adam_scalars* scalars_dev,
+                                 void* stream);
+
 /* All-gather into a temporary full view ([slide] note 原 N47 and beat b2;
  * [essay] ZeRO-3 的一次完整计算; [blog] 三级分片, ZeRO-3): the owners'
  * shards, concatenated in owner order, form the full per-layer view.

@@ -62,6 +62,31 @@ int main() {
   EXPECT(check_adam_scale((const float*)(b + 2046), p, m, v, b, 4096, e) == ZERO_ERR_ARG);  // inside bf16_out
   EXPECT(check_adam_scale(p + 4096, p, m, v, b, 4096, e) == ZERO_OK);            // just past master
   EXPECT(check_adam_scale(gr, p, m, v, b, 4096, e) == ZERO_OK);                  // inside the read-only gradient
+  // device scalars of the graph-capturable update
+  const zero_adam_scalars* sd = (const zero_adam_scalars*)P(0x700000);
+  EXPECT(check_adam_dev(p, m, v, b, gr, 4096, sd, e) == ZERO_OK);
+  EXPECT(check_adam_dev(p, m, v, b, gr, 4096, nullptr, e) == ZERO_ERR_ARG);
+  EXPECT(check_adam_dev(p, m, v, b, gr, 4096, (const zero_adam_scalars*)P(0x700002), e) == ZERO_ERR_ALIGN);
+  EXPECT(check_adam_dev(p, m, v, b, gr, 4096, (const zero_adam_scalars*)(v + 100), e) == ZERO_ERR_ARG);
+  EXPECT(check_adam_dev(p, m, v, b, gr, 4096, (const zero_adam_scalars*)(p + 4096 - 4), e) == ZERO_ERR_ARG);
+  EXPECT(check_adam_dev(p, m, v, b, gr, 4096, (const zero_adam_scalars*)(gr + 8), e) == ZERO_OK);
+  EXPECT(check_adam_dev(p, p + 16, v, b, gr, 4096, sd, e) == ZERO_ERR_ARG);   // buffers still checked
+  {
+    const uint16_t* gg[2] = {(const uint16_t*)P(0x10000), (const uint16_t*)P(0x20000)};
+    float wts[2] = {0.5f, 0.5f};
+    float* mp[2] = {(float*)P(0x100000), (float*)P(0x110000)};
+    float* mm[2] = {(float*)P(0x200000), (float*)P(0x210000)};
+    float* mv[2] = {(float*)P(0x300000), (float*)P(0x310000)};
+    uint16_t* mb[2] = {(uint16_t*)P(0x400000), (uint16_t*)P(0x410000)};
+    float* go[2] = {(float*)P(0x500000), (float*)P(0x510000)};
+    EXPECT(check_reduce_scatter_adam_dev(gg, wts, 2, 2048, 2, mp, mm, mv, mb, nullptr, go, sd, e) == ZERO_OK);
+    EXPECT(check_reduce_scatter_adam_dev(gg, wts, 2, 2048, 2, mp, mm, mv, mb, nullptr, go, nullptr, e) ==
+           ZERO_ERR_ARG);
+    EXPECT(check_reduce_scatter_adam_dev(gg, wts, 2, 2048, 2, mp, mm, mv, mb, nullptr, go,
+                                         (const zero_adam_scalars*)(go[1] + 10), e) == ZERO_ERR_ARG);
+    EXPECT(check_reduce_scatter_adam_dev(gg, wts, 2, 2048, 2, mp, mm, mv, mb, nullptr, go,
+                                         (const zero_adam_scalars*)(mb[0] + 2), e) == ZERO_ERR_ARG);
+  }
   // scalars
   zero_adam_scalars sc;
   EXPECT(adam_scalars(&hp, &sc, e) == ZERO_OK);

@@ -1,0 +1,146 @@
+"""GPU parity of the graph-capturable forms (the Adam scalars read from device
+memory when the kernels run):
+
+* zero_adam_shard_step_dev equals zero_adam_shard_step bit for bit, with and
+  without decay (decided in the kernel from the device value), on the vector
+  and element paths, with special values, with and without a gradient scale;
+* zero_reduce_scatter_adam_dev equals zero_reduce_scatter_adam;
+* a ShardedStep captured into a HIP graph and replayed over several steps
+  (new contributions and new step counts each time, eager work and
+  synchronisations between replays) equals the eager step after every replay;
+* invalid device-scalar arguments are rejected before anything is launched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as S
+from gpu_helpers import f32_to_dev
+
+pytestmark = pytest.mark.gpu
+
+z = pytest.importorskip("zero_sharded_optimizer_reduce_amd")
+from zero_sharded_optimizer_reduce_amd import _lib  # noqa: E402
+from zero_sharded_optimizer_reduce_amd.drivers import GraphedStep, ShardedStep  # noqa: E402
+
+
+def _hp(wd, t):
+    return dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=wd, step=t)
+
+
+def _bits(t):
+    return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
+
+
+def _same(a, b, what):
+    assert torch.equal(_bits(a), _bits(b)), what
+
+
+def _state(n, seed, special=False):
+    rng = np.random.default_rng(seed)
+    p = S.normal_f32(rng, n, 0.02)
+    m = S.normal_f32(rng, n, 1e-4)
+    v = np.abs(S.normal_f32(rng, n, 1e-6))
+    g = S.normal_f32(rng, n, 1e-3)
+    if special:
+        sv = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 1e-40, -1e-40, 3e38], np.float32)
+        p[:8], g[8:16], m[16:24] = sv, sv, sv
+        p[24:32], g[24:32] = -0.0, -0.0
+    return [f32_to_dev(x) for x in (p, m, v, g)]
+
+
+@pytest.mark.parametrize("n", [4096 * 3 + 4, 4096 + 3])
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+@pytest.mark.parametrize("scaled", [False, True])
+def test_update_with_device_scalars_equals_host_scalars(n, wd, scaled):
+    hp = _hp(wd, 5)
+    a = _state(n, 11, special=True)
+    b = [x.clone() for x in a]
+    ba = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    bb = torch.empty_like(ba)
+    scale = torch.tensor([0.37], device="cuda") if scaled else None
+    if scaled:
+        z.zero_adam_shard_step_scaled(a[0], a[1], a[2], ba, a[3], scale, hp)
+    else:
+        z.zero_adam_shard_step(a[0], a[1], a[2], ba, a[3], hp)
+    dev = z.adam_scalars_tensor(hp).cuda()
+    z.zero_adam_shard_step_dev(b[0], b[1], b[2], bb, b[3], dev, grad_scale=scale)
+    torch.cuda.synchronize()
+    for x, y, name in zip(a[:3] + [ba], b[:3] + [bb], ("master", "exp_avg", "exp_avg_sq", "bf16")):
+        _same(x, y, f"{name} n={n} wd={wd} scaled={scaled}")
+
+
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+@pytest.mark.parametrize("with_acc", [False, True])
+def test_fused_with_device_scalars_equals_host_scalars(wd, with_acc):
+    n, per = 4, 4096 + 4
+    grads = [S.bf16_normal(np.random.default_rng(r + 30), n * per, 1e-3) for r in range(n)]
+    gd = [torch.from_numpy(g.view(np.int16)).cuda().view(torch.bfloat16) for g in grads]
+    w = oracle.weights_from_counts([3, 5, 2, 7])
+    hp = _hp(wd, 9)
+    sets = []
+    for _ in range(2):
+        st = [_state(per, 40 + k) for k in range(n)]
+        sets.append(dict(p=[s[0] for s in st], m=[s[1] for s in st], v=[s[2] for s in st],
+                         b=[torch.empty(per, dtype=torch.bfloat16, device="cuda") for _ in range(n)],
+                         g=[torch.empty(per, device="cuda") for _ in range(n)],
+                         acc=[s[3] for s in st] if with_acc else None))
+    A, B = sets
+    z.zero_reduce_scatter_adam(gd, w, A["p"], A["m"], A["v"], A["b"], hp, grad_out=A["g"], grad_acc=A["acc"])
+    z.zero_reduce_scatter_adam_dev(gd, w, B["p"], B["m"], B["v"], B["b"], z.adam_scalars_tensor(hp).cuda(),
+                                   grad_out=B["g"], grad_acc=B["acc"])
+    torch.cuda.synchronize()
+    for key in ("p", "m", "v", "b", "g"):
+        for k in range(n):
+            _same(A[key][k], B[key][k], f"{key}[{k}]")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_replays_equal_eager_steps(fused):
+    numels = [4096 * 7, 1000, 4096 * 3 + 12]
+    n = 4
+    gen = S.DeviceGen(77)
+    eager, graphed = ShardedStep(numels, n), ShardedStep(numels, n)
+    master0 = gen.normal_(torch.empty(eager.psi_pad, device="cuda"), 0.02, 0)
+    eager.load_master(master0)
+    graphed.load_master(master0)
+    w = z.zero_rank_weights([4096, 3072, 4096, 2048], n)
+    grads = [torch.empty(eager.psi_pad, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    tmp = torch.empty(eager.psi_pad, device="cuda")
+    g = GraphedStep(graphed, grads, w, fused=fused)
+    for t in range(1, 6):
+        for r in range(n):
+            gen.bf16_normal_(grads[r], 1e-3, t, r, tmp=tmp)
+        hp = _hp(0.1 if t % 2 else 0.0, t)
+        eager.step(grads, w, hp)
+        g.step(hp)
+        torch.cuda.synchronize()
+        for name in ("master", "exp_avg", "exp_avg_sq", "bf16", "grad"):
+            for k in range(n):
+                _same(getattr(eager, name)[k], getattr(graphed, name)[k], f"step {t} {name}[{k}]")
+        _same(eager.view, graphed.view, f"step {t} view")
+        # unrelated eager work and a synchronisation before the next replay
+        tmp.mul_(0.5).add_(1.0)
+        torch.cuda.synchronize()
+
+
+def test_device_scalar_arguments_are_validated():
+    lib = z.load()
+    n = 1024
+    p, m, v, g = (torch.zeros(n, device="cuda") for _ in range(4))
+    b = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    dev = z.adam_scalars_tensor(_hp(0.0, 1)).cuda()
+    ptr = [t.data_ptr() for t in (p, m, v, b, g)]
+    assert lib.zero_adam_shard_step_dev(*ptr, None, n, None, None) == _lib.ZERO_ERR_ARG
+    assert lib.zero_adam_shard_step_dev(*ptr, None, n, dev.data_ptr() + 2, None) == _lib.ZERO_ERR_ALIGN
+    with pytest.raises(z.ZeroError, match="ZERO_ERR_ARG"):      # the scalars inside an output
+        z.zero_adam_shard_step_dev(p, m, v, b, g, m[100:100 + z.ADAM_SCALARS_FLOATS])
+    with pytest.raises(ValueError):
+        z.zero_adam_shard_step_dev(p, m, v, b, g, dev[:4])
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(p) == 0 and torch.count_nonzero(m) == 0
+    # the same scalars in the read-only gradient are allowed
+    g[:z.ADAM_SCALARS_FLOATS] = dev
+    z.zero_adam_shard_step_dev(p, m, v, b, g, g[:z.ADAM_SCALARS_FLOATS])
+    torch.cuda.synchronize()

@@ -7,9 +7,12 @@ that sequence its calls.
 """
 from ._lib import ZERO_OFFLOAD_ADAM, ZERO_OFFLOAD_REDUCE, ZERO_OFFLOAD_REDUCE_ADAM, ZeroError, load  # noqa: F401
 from .api import (  # noqa: F401
+    ADAM_SCALARS_FLOATS,
     ZeroOffload,
+    adam_scalars_tensor,
     zero_adam_scalars_compute,
     zero_adam_shard_step,
+    zero_adam_shard_step_dev,
     zero_adam_shard_step_scaled,
     zero_all_gather_layer,
     zero_grad_norm_sq,
@@ -21,6 +24,7 @@ from .api import (  # noqa: F401
     zero_rank_weights,
     zero_reduce_scatter,
     zero_reduce_scatter_adam,
+    zero_reduce_scatter_adam_dev,
     zero_reduce_scatter_f32,
     zero_shard_layout,
 )

@@ -165,6 +165,39 @@ def zero_grad_norm_sq(shards: Sequence[torch.Tensor], workspace: torch.Tensor, n
                                    _stream(stream)), "zero_grad_norm_sq")
 
 
+def _fused_args(name, rank_grads, rank_weights, master, exp_avg, exp_avg_sq, bf16_out, grad_out, grad_acc):
+    n_ranks, n_shards = len(rank_grads), len(master)
+    if n_ranks < 1 or n_shards < 1:
+        raise ValueError(f"{name}: need at least one rank and one owner")
+    numel = rank_grads[0].numel()
+    gp = [_dev(g, f"rank_grads[{r}]", _BF16_LIKE) for r, g in enumerate(rank_grads)]
+    if any(g.numel() != numel for g in rank_grads):
+        raise ValueError(f"{name}: rank contributions differ in size")
+    if numel % n_shards:
+        raise ValueError(f"{name}: numel not divisible by the number of owners")
+    s = numel // n_shards
+    tables = []
+    for tname, ts, dt in (("master", master, (torch.float32,)), ("exp_avg", exp_avg, (torch.float32,)),
+                          ("exp_avg_sq", exp_avg_sq, (torch.float32,)), ("bf16_out", bf16_out, _BF16_LIKE)):
+        if len(ts) != n_shards or any(t.numel() != s for t in ts):
+            raise ValueError(f"{name}: {tname} needs {n_shards} tensors of {s} elements")
+        tables.append(_ptrs([_dev(t, f"{tname}[{k}]", dt) for k, t in enumerate(ts)]))
+    go = None
+    if grad_out is not None:
+        if len(grad_out) != n_shards or any(t.numel() != s for t in grad_out):
+            raise ValueError(f"{name}: grad_out needs one tensor per owner")
+        go = _ptrs([_dev(t, f"grad_out[{k}]", (torch.float32,)) for k, t in enumerate(grad_out)])
+    ga = None
+    if grad_acc is not None:
+        if len(grad_acc) != n_shards or any(t.numel() != s for t in grad_acc):
+            raise ValueError(f"{name}: grad_acc needs one tensor per owner")
+        ga = _ptrs([_dev(t, f"grad_acc[{k}]", (torch.float32,)) for k, t in enumerate(grad_acc)])
+    w = np.ascontiguousarray(np.asarray(rank_weights, dtype=np.float32))
+    if w.size != n_ranks:
+        raise ValueError(f"{name}: one weight per rank")
+    return (_ptrs(gp), w, n_ranks, numel, n_shards, tables, ga, go)
+
+
 def zero_reduce_scatter_adam(rank_grads: Sequence[torch.Tensor], rank_weights, master, exp_avg, exp_avg_sq,
                              bf16_out, hp, grad_out=None, grad_acc=None, stream=None) -> None:
     """Fused reduce-scatter + owner Adam update: for each owner k, the reduced
@@ -173,39 +206,70 @@ def zero_reduce_scatter_adam(rank_grads: Sequence[torch.Tensor], rank_weights, m
     (optional list) receives the gradient used.  Bit-identical to
     zero_reduce_scatter (accumulate mode with grad_acc) followed by
     zero_adam_shard_step on every owner."""
-    n_ranks, n_shards = len(rank_grads), len(master)
-    if n_ranks < 1 or n_shards < 1:
-        raise ValueError("zero_reduce_scatter_adam: need at least one rank and one owner")
-    numel = rank_grads[0].numel()
-    gp = [_dev(g, f"rank_grads[{r}]", _BF16_LIKE) for r, g in enumerate(rank_grads)]
-    if any(g.numel() != numel for g in rank_grads):
-        raise ValueError("zero_reduce_scatter_adam: rank contributions differ in size")
-    if numel % n_shards:
-        raise ValueError("zero_reduce_scatter_adam: numel not divisible by the number of owners")
-    s = numel // n_shards
-    tables = []
-    for name, ts, dt in (("master", master, (torch.float32,)), ("exp_avg", exp_avg, (torch.float32,)),
-                         ("exp_avg_sq", exp_avg_sq, (torch.float32,)), ("bf16_out", bf16_out, _BF16_LIKE)):
-        if len(ts) != n_shards or any(t.numel() != s for t in ts):
-            raise ValueError(f"zero_reduce_scatter_adam: {name} needs {n_shards} tensors of {s} elements")
-        tables.append(_ptrs([_dev(t, f"{name}[{k}]", dt) for k, t in enumerate(ts)]))
-    go = None
-    if grad_out is not None:
-        if len(grad_out) != n_shards or any(t.numel() != s for t in grad_out):
-            raise ValueError("zero_reduce_scatter_adam: grad_out needs one tensor per owner")
-        go = _ptrs([_dev(t, f"grad_out[{k}]", (torch.float32,)) for k, t in enumerate(grad_out)])
-    ga = None
-    if grad_acc is not None:
-        if len(grad_acc) != n_shards or any(t.numel() != s for t in grad_acc):
-            raise ValueError("zero_reduce_scatter_adam: grad_acc needs one tensor per owner")
-        ga = _ptrs([_dev(t, f"grad_acc[{k}]", (torch.float32,)) for k, t in enumerate(grad_acc)])
-    w = np.ascontiguousarray(np.asarray(rank_weights, dtype=np.float32))
-    if w.size != n_ranks:
-        raise ValueError("zero_reduce_scatter_adam: one weight per rank")
+    gp, w, n_ranks, numel, n_shards, tables, ga, go = _fused_args(
+        "zero_reduce_scatter_adam", rank_grads, rank_weights, master, exp_avg, exp_avg_sq, bf16_out, grad_out,
+        grad_acc)
     h = hparams(hp)
-    check(load().zero_reduce_scatter_adam(_ptrs(gp), w.ctypes.data_as(_lib.FP), n_ranks, numel, n_shards,
+    check(load().zero_reduce_scatter_adam(gp, w.ctypes.data_as(_lib.FP), n_ranks, numel, n_shards,
                                           *tables, ga, go, C.byref(h), _stream(stream)),
           "zero_reduce_scatter_adam")
+
+
+# ------------------------------------------------------------ graph-capturable forms
+ADAM_SCALARS_FLOATS = len(_lib.AdamScalars._fields_)
+
+
+def adam_scalars_tensor(hp, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The step's scalars (zero_adam_scalars_compute) as a float32 tensor in the
+    struct's field order, ready to be copied into the device struct that the
+    _dev calls read.  out: an existing CPU float32 tensor to fill (e.g. pinned)."""
+    sc = _lib.AdamScalars()
+    check(load().zero_adam_scalars_compute(C.byref(hparams(hp)), C.byref(sc)), "zero_adam_scalars_compute")
+    vals = [getattr(sc, f) for f, _ in _lib.AdamScalars._fields_]
+    if out is None:
+        return torch.tensor(vals, dtype=torch.float32)
+    if out.device.type != "cpu" or out.dtype != torch.float32 or out.numel() < ADAM_SCALARS_FLOATS:
+        raise ValueError("adam_scalars_tensor: out must be a CPU float32 tensor of >= 9 elements")
+    out.numpy()[:ADAM_SCALARS_FLOATS] = np.array(vals, dtype=np.float32)
+    return out
+
+
+def _scalars_dev(scalars_dev: torch.Tensor) -> int:
+    ptr = _dev(scalars_dev, "scalars_dev", (torch.float32,))
+    if scalars_dev.numel() < ADAM_SCALARS_FLOATS:
+        raise ValueError(f"scalars_dev: needs {ADAM_SCALARS_FLOATS} float32 elements")
+    return ptr
+
+
+def zero_adam_shard_step_dev(master, exp_avg, exp_avg_sq, bf16_out, grad, scalars_dev: torch.Tensor,
+                             grad_scale: Optional[torch.Tensor] = None, stream=None) -> None:
+    """zero_adam_shard_step with the step's scalars read from scalars_dev (a
+    device float32 tensor holding adam_scalars_tensor(hp)) when the kernel runs,
+    so that a captured graph replays with new scalars; grad_scale as in
+    zero_adam_shard_step_scaled, or None."""
+    n = master.numel()
+    ptrs = [_dev(master, "master", (torch.float32,)), _dev(exp_avg, "exp_avg", (torch.float32,)),
+            _dev(exp_avg_sq, "exp_avg_sq", (torch.float32,)), _dev(bf16_out, "bf16_out", _BF16_LIKE),
+            _dev(grad, "grad", (torch.float32,))]
+    if any(t.numel() != n for t in (exp_avg, exp_avg_sq, bf16_out, grad)):
+        raise ValueError("zero_adam_shard_step_dev: all buffers must have the same numel")
+    gs = None
+    if grad_scale is not None:
+        gs = _dev(grad_scale, "grad_scale", (torch.float32,))
+    check(load().zero_adam_shard_step_dev(*ptrs, gs, n, _scalars_dev(scalars_dev), _stream(stream)),
+          "zero_adam_shard_step_dev")
+
+
+def zero_reduce_scatter_adam_dev(rank_grads, rank_weights, master, exp_avg, exp_avg_sq, bf16_out,
+                                 scalars_dev: torch.Tensor, grad_out=None, grad_acc=None, stream=None) -> None:
+    """zero_reduce_scatter_adam with the step's scalars read from scalars_dev
+    when the kernels run (see zero_adam_shard_step_dev)."""
+    gp, w, n_ranks, numel, n_shards, tables, ga, go = _fused_args(
+        "zero_reduce_scatter_adam_dev", rank_grads, rank_weights, master, exp_avg, exp_avg_sq, bf16_out,
+        grad_out, grad_acc)
+    check(load().zero_reduce_scatter_adam_dev(gp, w.ctypes.data_as(_lib.FP), n_ranks, numel, n_shards,
+                                              *tables, ga, go, _scalars_dev(scalars_dev), _stream(stream)),
+          "zero_reduce_scatter_adam_dev")
 
 
 def zero_all_gather_layer(shards: Sequence[torch.Tensor], full_view: torch.Tensor, stream=None) -> None:

@@ -27,6 +27,7 @@ struct AdamParams {
   const float* gscale;  // device scalar multiplying g (gradient clipping), or NULL
   int64_t n;
   zero_adam_scalars s;
+  const zero_adam_scalars* sdev;  // device copy of the scalars (read when the kernel runs), or NULL
 };
 
 // Fixed number of partial sums per shard for the gradient norm, so that the
@@ -56,6 +57,7 @@ struct FusedParams {
   int64_t shard;
   int n_ranks;
   zero_adam_scalars s;
+  const zero_adam_scalars* sdev;  // device copy of the scalars, or NULL
 };
 
 struct GatherParams {

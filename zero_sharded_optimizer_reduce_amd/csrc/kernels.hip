@@ -177,7 +177,17 @@ __global__ __launch_bounds__(kBlock) void rs_scalar_kernel(RsParams p) {
 // The owner's update of its master weight p, first moment m and second moment
 // v with the reduced gradient g (slide, note 原 N48; essay "把训练账本放进多张
 // 设备", section 从持久状态开始记账): bias-corrected Adam with decoupled decay.
-template <bool WD>
+// WD: 0 no decay term, 1 decay term, 2 the scalars come from device memory and
+// the term is applied when their weight_decay is non-zero (a uniform branch),
+// exactly as the host decides it for 0 and 1.
+template <int WD>
+__device__ __forceinline__ zero_adam_scalars step_scalars(const zero_adam_scalars& by_value,
+                                                          const zero_adam_scalars* dev) {
+  if (WD == 2) return *dev;
+  return by_value;
+}
+
+template <int WD>
 __device__ __forceinline__ void adam_elem(float& p, float& m, float& v, float g,
                                           const zero_adam_scalars& s) {
   const float m1 = s.beta1 * m + s.one_minus_beta1 * g;
@@ -187,7 +197,7 @@ __device__ __forceinline__ void adam_elem(float& p, float& m, float& v, float g,
   const float v_hat = v1 / s.bias_correction2;
   const float denom = sqrtf(v_hat) + s.eps;
   float u = m_hat / denom;
-  if (WD) u = u + s.weight_decay * p;
+  if (WD == 1 || (WD == 2 && s.weight_decay != 0.0f)) u = u + s.weight_decay * p;
   p = p - s.lr * u;
   m = m1;
   v = v1;
@@ -197,8 +207,9 @@ __device__ __forceinline__ void adam_elem(float& p, float& m, float& v, float g,
 // weight (14 B/param).  Vector path: 4 elements per 16-byte access, U vectors
 // per lane per iteration; the n % 4 tail goes element-wise.  SC: the gradient
 // is first multiplied by the device scalar *gscale (the clip coefficient).
-template <bool WD, bool SC, int U, int BS>
+template <int WD, bool SC, int U, int BS>
 __global__ __launch_bounds__(BS) void adam_vec_kernel(AdamParams a) {
+  const zero_adam_scalars s = step_scalars<WD>(a.s, a.sdev);
   const int64_t nvec = a.n >> 2;
   f32x4* __restrict__ P = reinterpret_cast<f32x4*>(a.p);
   f32x4* __restrict__ M = reinterpret_cast<f32x4*>(a.m);
@@ -230,7 +241,7 @@ __global__ __launch_bounds__(BS) void adam_vec_kernel(AdamParams a) {
       float ve[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
       const float ge[4] = {g[u].x, g[u].y, g[u].z, g[u].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) adam_elem<WD>(pe[e], me[e], ve[e], ge[e], a.s);
+      for (int e = 0; e < 4; ++e) adam_elem<WD>(pe[e], me[e], ve[e], ge[e], s);
       st_nt(f32x4{pe[0], pe[1], pe[2], pe[3]}, P + i);
       st_nt(f32x4{me[0], me[1], me[2], me[3]}, M + i);
       st_nt(f32x4{ve[0], ve[1], ve[2], ve[3]}, V + i);
@@ -241,7 +252,7 @@ __global__ __launch_bounds__(BS) void adam_vec_kernel(AdamParams a) {
   if (blockIdx.x == 0 && threadIdx.x < tail) {
     const int64_t i = (nvec << 2) + threadIdx.x;
     float pe = a.p[i], me = a.m[i], ve = a.v[i];
-    adam_elem<WD>(pe, me, ve, SC ? a.g[i] * c : a.g[i], a.s);
+    adam_elem<WD>(pe, me, ve, SC ? a.g[i] * c : a.g[i], s);
     a.p[i] = pe;
     a.m[i] = me;
     a.v[i] = ve;
@@ -249,13 +260,14 @@ __global__ __launch_bounds__(BS) void adam_vec_kernel(AdamParams a) {
   }
 }
 
-template <bool WD, bool SC>
+template <int WD, bool SC>
 __global__ __launch_bounds__(kBlock) void adam_scalar_kernel(AdamParams a) {
+  const zero_adam_scalars s = step_scalars<WD>(a.s, a.sdev);
   const float c = SC ? *a.gscale : 1.0f;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < a.n;
        i += static_cast<int64_t>(gridDim.x) * kBlock) {
     float pe = a.p[i], me = a.m[i], ve = a.v[i];
-    adam_elem<WD>(pe, me, ve, SC ? a.g[i] * c : a.g[i], a.s);
+    adam_elem<WD>(pe, me, ve, SC ? a.g[i] * c : a.g[i], s);
     a.p[i] = pe;
     a.m[i] = me;
     a.v[i] = ve;
@@ -348,8 +360,9 @@ __global__ __launch_bounds__(kBlock) void norm_final_kernel(NormParams p) {
 // micro-batch of an accumulation updates directly).  Bytes per parameter
 // (N=4): 8 (contributions) + 12 (state) read, 12 (state) + 2 (BF16) written
 // = 34, against 12 + 30 = 42 for the two kernels.
-template <int N, bool WD, bool WG, bool ACC, int U, int BS>
+template <int N, int WD, bool WG, bool ACC, int U, int BS>
 __global__ __launch_bounds__(BS) void fused_vec_kernel(FusedParams p) {
+  const zero_adam_scalars s = step_scalars<WD>(p.s, p.sdev);
   constexpr int NMAX = N > 0 ? N : ZERO_MAX_RANKS;
   const int n = N > 0 ? N : p.n_ranks;
   const int k = blockIdx.y;
@@ -391,7 +404,7 @@ __global__ __launch_bounds__(BS) void fused_vec_kernel(FusedParams p) {
       float ve[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
       const float ge[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) adam_elem<WD>(pe[e], me[e], ve[e], ge[e], p.s);
+      for (int e = 0; e < 4; ++e) adam_elem<WD>(pe[e], me[e], ve[e], ge[e], s);
       st_nt(f32x4{pe[0], pe[1], pe[2], pe[3]}, P + i);
       st_nt(f32x4{me[0], me[1], me[2], me[3]}, M + i);
       st_nt(f32x4{ve[0], ve[1], ve[2], ve[3]}, V + i);
@@ -400,8 +413,9 @@ __global__ __launch_bounds__(BS) void fused_vec_kernel(FusedParams p) {
   }
 }
 
-template <bool WD>
+template <int WD>
 __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(FusedParams p) {
+  const zero_adam_scalars s = step_scalars<WD>(p.s, p.sdev);
   const int k = blockIdx.y;
   const int64_t base = static_cast<int64_t>(k) * p.shard;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < p.shard;
@@ -411,7 +425,7 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(FusedParams p) {
     if (p.gacc[k]) g = p.gacc[k][i] + g;
     if (p.gout[k]) p.gout[k][i] = g;
     float pe = p.p[k][i], me = p.m[k][i], ve = p.v[k][i];
-    adam_elem<WD>(pe, me, ve, g, p.s);
+    adam_elem<WD>(pe, me, ve, g, s);
     p.p[k][i] = pe;
     p.m[k][i] = me;
     p.v[k][i] = ve;
@@ -605,7 +619,7 @@ hipError_t launch_reduce_scatter_f32(const RsParams& p, int n_shards, bool accum
                     : rs_f32_dispatch<false>(p, n_shards, vec, stream);
 }
 
-template <int N, bool WD, bool WG, bool ACC>
+template <int N, int WD, bool WG, bool ACC>
 hipError_t fused_vec_launch(const FusedParams& p, int n_shards, hipStream_t s) {
   dim3 grid(grid_x(p.shard >> 2, kFusedU, n_shards, kFusedBlock), n_shards);
   hipLaunchKernelGGL((fused_vec_kernel<N, WD, WG, ACC, kFusedU, kFusedBlock>), grid, dim3(kFusedBlock),
@@ -613,7 +627,7 @@ hipError_t fused_vec_launch(const FusedParams& p, int n_shards, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool WD, bool WG, bool ACC>
+template <int WD, bool WG, bool ACC>
 hipError_t fused_dispatch_n(const FusedParams& p, int n_shards, hipStream_t s) {
   switch (p.n_ranks) {
     case 1: return fused_vec_launch<1, WD, WG, ACC>(p, n_shards, s);
@@ -624,19 +638,30 @@ hipError_t fused_dispatch_n(const FusedParams& p, int n_shards, hipStream_t s) {
   }
 }
 
-template <bool WD, bool WG>
-hipError_t fused_dispatch_acc(const FusedParams& p, int n_shards, bool acc, hipStream_t s) {
-  return acc ? fused_dispatch_n<WD, WG, true>(p, n_shards, s) : fused_dispatch_n<WD, WG, false>(p, n_shards, s);
+template <int WD>
+hipError_t fused_dispatch_wd(const FusedParams& p, bool write_grad, bool acc, hipStream_t s) {
+  if (write_grad)
+    return acc ? fused_dispatch_n<WD, true, true>(p, 1, s) : fused_dispatch_n<WD, true, false>(p, 1, s);
+  return acc ? fused_dispatch_n<WD, false, true>(p, 1, s) : fused_dispatch_n<WD, false, false>(p, 1, s);
+}
+
+// The decay mode of the update kernels: 2 when the scalars are read from
+// device memory (decided in the kernel), else 1 or 0 from the host value.
+int decay_mode(const zero_adam_scalars& s, const zero_adam_scalars* sdev) {
+  if (sdev) return 2;
+  return s.weight_decay != 0.0f ? 1 : 0;
 }
 
 hipError_t launch_fused(const FusedParams& p, int n_shards, bool write_grad, bool vec, hipStream_t s) {
-  const bool wd = p.s.weight_decay != 0.0f;
+  const int wd = decay_mode(p.s, p.sdev);
   if (!vec) {
     dim3 grid(grid_x(p.shard, 1, n_shards), n_shards);
-    if (wd)
-      hipLaunchKernelGGL((fused_scalar_kernel<true>), grid, dim3(kBlock), 0, s, p);
+    if (wd == 2)
+      hipLaunchKernelGGL((fused_scalar_kernel<2>), grid, dim3(kBlock), 0, s, p);
+    else if (wd == 1)
+      hipLaunchKernelGGL((fused_scalar_kernel<1>), grid, dim3(kBlock), 0, s, p);
     else
-      hipLaunchKernelGGL((fused_scalar_kernel<false>), grid, dim3(kBlock), 0, s, p);
+      hipLaunchKernelGGL((fused_scalar_kernel<0>), grid, dim3(kBlock), 0, s, p);
     return hipGetLastError();
   }
   const bool acc = p.gacc[0] != nullptr;
@@ -653,16 +678,18 @@ hipError_t launch_fused(const FusedParams& p, int n_shards, bool write_grad, boo
     q.gout[0] = p.gout[k];
     q.gacc[0] = p.gacc[k];
     hipError_t err;
-    if (wd)
-      err = write_grad ? fused_dispatch_acc<true, true>(q, 1, acc, s) : fused_dispatch_acc<true, false>(q, 1, acc, s);
+    if (wd == 2)
+      err = fused_dispatch_wd<2>(q, write_grad, acc, s);
+    else if (wd == 1)
+      err = fused_dispatch_wd<1>(q, write_grad, acc, s);
     else
-      err = write_grad ? fused_dispatch_acc<false, true>(q, 1, acc, s) : fused_dispatch_acc<false, false>(q, 1, acc, s);
+      err = fused_dispatch_wd<0>(q, write_grad, acc, s);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
 }
 
-template <bool WD, bool SC>
+template <int WD, bool SC>
 hipError_t adam_launch(const AdamParams& a, bool vec, hipStream_t s) {
   if (vec) {
     dim3 grid(grid_x(a.n >> 2, kAdamU, 1, kAdamBlock));
@@ -675,11 +702,16 @@ hipError_t adam_launch(const AdamParams& a, bool vec, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int WD>
+hipError_t adam_launch_sc(const AdamParams& a, bool vec, hipStream_t s) {
+  return a.gscale ? adam_launch<WD, true>(a, vec, s) : adam_launch<WD, false>(a, vec, s);
+}
+
 hipError_t launch_adam(const AdamParams& a, bool vec, hipStream_t s) {
-  const bool wd = a.s.weight_decay != 0.0f;
-  const bool sc = a.gscale != nullptr;
-  if (wd) return sc ? adam_launch<true, true>(a, vec, s) : adam_launch<true, false>(a, vec, s);
-  return sc ? adam_launch<false, true>(a, vec, s) : adam_launch<false, false>(a, vec, s);
+  const int wd = decay_mode(a.s, a.sdev);
+  if (wd == 2) return adam_launch_sc<2>(a, vec, s);
+  if (wd == 1) return adam_launch_sc<1>(a, vec, s);
+  return adam_launch_sc<0>(a, vec, s);
 }
 
 hipError_t launch_norm(NormParams& p, bool vec, hipStream_t s) {

@@ -78,6 +78,40 @@ int check_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* ra
                               float* const* grad_out, const zero_adam_hparams* hp, Err& e) {
   int st = check_adam_hparams(hp, e);
   if (st) return st;
+  return check_reduce_scatter_adam_buffers(rank_grads, rank_weights, n_ranks, numel, n_shards, master,
+                                           exp_avg, exp_avg_sq, bf16_out, grad_acc, grad_out, e);
+}
+
+int check_reduce_scatter_adam_dev(const uint16_t* const* rank_grads, const float* rank_weights,
+                                  int n_ranks, int64_t numel, int n_shards, float* const* master,
+                                  float* const* exp_avg, float* const* exp_avg_sq,
+                                  uint16_t* const* bf16_out, const float* const* grad_acc,
+                                  float* const* grad_out, const zero_adam_scalars* scalars_dev, Err& e) {
+  int st = check_reduce_scatter_adam_buffers(rank_grads, rank_weights, n_ranks, numel, n_shards, master,
+                                             exp_avg, exp_avg_sq, bf16_out, grad_acc, grad_out, e);
+  if (st) return st;
+  if (!scalars_dev) return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: NULL device scalars");
+  if (reinterpret_cast<uintptr_t>(scalars_dev) & 3u)
+    return set_err(e, ZERO_ERR_ALIGN, "reduce_scatter_adam: device scalars not 4-byte aligned");
+  if (numel == 0) return ZERO_OK;
+  const int64_t shard = numel / n_shards;
+  const Range sc = range_of(scalars_dev, sizeof(zero_adam_scalars));
+  for (int k = 0; k < n_shards; ++k) {
+    const Range outs[5] = {range_of(master[k], shard * 4), range_of(exp_avg[k], shard * 4),
+                           range_of(exp_avg_sq[k], shard * 4), range_of(bf16_out[k], shard * 2),
+                           range_of(grad_out ? grad_out[k] : nullptr, grad_out ? shard * 4 : 0)};
+    for (const Range& r : outs)
+      if (overlaps(sc, r))
+        return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: device scalars overlap an output of owner %d", k);
+  }
+  return ZERO_OK;
+}
+
+int check_reduce_scatter_adam_buffers(const uint16_t* const* rank_grads, const float* rank_weights,
+                                      int n_ranks, int64_t numel, int n_shards, float* const* master,
+                                      float* const* exp_avg, float* const* exp_avg_sq,
+                                      uint16_t* const* bf16_out, const float* const* grad_acc,
+                                      float* const* grad_out, Err& e) {
   if (!rank_grads || !rank_weights || !master || !exp_avg || !exp_avg_sq || !bf16_out)
     return set_err(e, ZERO_ERR_ARG, "reduce_scatter_adam: NULL pointer table or weights");
   if (n_ranks < 1 || n_ranks > ZERO_MAX_RANKS)
@@ -195,6 +229,28 @@ int check_adam(const float* master, const float* exp_avg, const float* exp_avg_s
                const zero_adam_hparams* hp, Err& e) {
   int st = check_adam_hparams(hp, e);
   if (st) return st;
+  return check_adam_buffers(master, exp_avg, exp_avg_sq, bf16_out, grad, n, e);
+}
+
+int check_adam_dev(const float* master, const float* exp_avg, const float* exp_avg_sq,
+                   const uint16_t* bf16_out, const float* grad, int64_t n,
+                   const zero_adam_scalars* scalars_dev, Err& e) {
+  int st = check_adam_buffers(master, exp_avg, exp_avg_sq, bf16_out, grad, n, e);
+  if (st) return st;
+  if (!scalars_dev) return set_err(e, ZERO_ERR_ARG, "adam: NULL device scalars");
+  if (reinterpret_cast<uintptr_t>(scalars_dev) & 3u)
+    return set_err(e, ZERO_ERR_ALIGN, "adam: device scalars not 4-byte aligned");
+  if (n == 0) return ZERO_OK;
+  const Range sc = range_of(scalars_dev, sizeof(zero_adam_scalars));
+  const Range outs[4] = {range_of(master, n * 4), range_of(exp_avg, n * 4), range_of(exp_avg_sq, n * 4),
+                         range_of(bf16_out, n * 2)};
+  for (const Range& r : outs)
+    if (overlaps(sc, r)) return set_err(e, ZERO_ERR_ARG, "adam: device scalars overlap a buffer the update writes");
+  return ZERO_OK;
+}
+
+int check_adam_buffers(const float* master, const float* exp_avg, const float* exp_avg_sq,
+                       const uint16_t* bf16_out, const float* grad, int64_t n, Err& e) {
   if (n < 0) return set_err(e, ZERO_ERR_ARG, "adam: n=%lld < 0", (long long)n);
   if (n == 0) return ZERO_OK;  // touches no buffer; NULL pointers allowed
   if (!master || !exp_avg || !exp_avg_sq || !bf16_out || !grad)

@@ -34,6 +34,24 @@ int check_adam(const float* master, const float* exp_avg, const float* exp_avg_s
                const uint16_t* bf16_out, const float* grad, int64_t n,
                const zero_adam_hparams* hp, Err& e);
 
+// The same checks without the hyper-parameters (buffers only), and the
+// device-scalar forms: the scalars non-NULL, 4-byte aligned, outside every
+// buffer the update writes.
+int check_adam_buffers(const float* master, const float* exp_avg, const float* exp_avg_sq,
+                       const uint16_t* bf16_out, const float* grad, int64_t n, Err& e);
+int check_adam_dev(const float* master, const float* exp_avg, const float* exp_avg_sq,
+                   const uint16_t* bf16_out, const float* grad, int64_t n,
+                   const zero_adam_scalars* scalars_dev, Err& e);
+int check_reduce_scatter_adam_buffers(const uint16_t* const* rank_grads, const float* rank_weights,
+                                      int n_ranks, int64_t numel, int n_shards, float* const* master,
+                                      float* const* exp_avg, float* const* exp_avg_sq,
+                                      uint16_t* const* bf16_out, const float* const* grad_acc,
+                                      float* const* grad_out, Err& e);
+int check_reduce_scatter_adam_dev(const uint16_t* const* rank_grads, const float* rank_weights,
+                                  int n_ranks, int64_t numel, int n_shards, float* const* master,
+                                  float* const* exp_avg, float* const* exp_avg_sq,
+                                  uint16_t* const* bf16_out, const float* const* grad_acc,
+                                  float* const* grad_out, const zero_adam_scalars* scalars_dev, Err& e);
 // The device scale of zero_adam_shard_step_scaled: non-NULL, 4-byte aligned,
 // outside every buffer the update writes.
 int check_adam_scale(const float* grad_scale, const float* master, const float* exp_avg,

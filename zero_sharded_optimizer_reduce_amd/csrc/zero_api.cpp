@@ -189,21 +189,44 @@ int zero_grad_norm_sq(const float* const* shards, int n_shards, int64_t shard_nu
   return hip_status(launch_norm(p, vec, static_cast<hipStream_t>(stream)), "zero_grad_norm_sq");
 }
 
-int zero_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* rank_weights,
-                             int n_ranks, int64_t numel, int n_shards, float* const* master,
-                             float* const* exp_avg, float* const* exp_avg_sq,
-                             uint16_t* const* bf16_out, const float* const* grad_acc,
-                             float* const* grad_out, const zero_adam_hparams* hp, void* stream) {
+int zero_adam_shard_step_dev(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* bf16_out,
+                             const float* grad, const float* grad_scale, int64_t n,
+                             const zero_adam_scalars* scalars_dev, void* stream) {
   Err e;
-  int st = check_reduce_scatter_adam(rank_grads, rank_weights, n_ranks, numel, n_shards, master,
-                                     exp_avg, exp_avg_sq, bf16_out, grad_acc, grad_out, hp, e);
+  int st = check_adam_dev(master, exp_avg, exp_avg_sq, bf16_out, grad, n, scalars_dev, e);
   if (st) return fail(st, e.msg);
-  if (numel == 0) return ZERO_OK;
+  if (n == 0) return ZERO_OK;
+  if (grad_scale) {
+    st = check_adam_scale(grad_scale, master, exp_avg, exp_avg_sq, bf16_out, n, e);
+    if (st) return fail(st, e.msg);
+  }
+  AdamParams a;
+  memset(&a, 0, sizeof a);
+  a.p = master;
+  a.m = exp_avg;
+  a.v = exp_avg_sq;
+  a.b = bf16_out;
+  a.g = grad;
+  a.gscale = grad_scale;
+  a.n = n;
+  a.sdev = scalars_dev;
+  const bool vec = aligned16(master) && aligned16(exp_avg) && aligned16(exp_avg_sq) &&
+                   aligned16(grad) && aligned8(bf16_out);
+  set_path(vec);
+  return hip_status(launch_adam(a, vec, static_cast<hipStream_t>(stream)), "zero_adam_shard_step_dev");
+}
+
+static int fused_common(const uint16_t* const* rank_grads, const float* rank_weights, int n_ranks,
+                        int64_t numel, int n_shards, float* const* master, float* const* exp_avg,
+                        float* const* exp_avg_sq, uint16_t* const* bf16_out,
+                        const float* const* grad_acc, float* const* grad_out, const zero_adam_scalars& s,
+                        const zero_adam_scalars* sdev, void* stream, const char* where) {
   FusedParams p;
   memset(&p, 0, sizeof p);
   p.shard = numel / n_shards;
   p.n_ranks = n_ranks;
-  adam_scalars(hp, &p.s, e);
+  p.s = s;
+  p.sdev = sdev;
   bool vec = (p.shard % 4) == 0;
   for (int r = 0; r < n_ranks; ++r) {
     p.g[r] = rank_grads[r];
@@ -222,7 +245,40 @@ int zero_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* ran
   }
   set_path(vec);
   return hip_status(launch_fused(p, n_shards, grad_out != nullptr, vec, static_cast<hipStream_t>(stream)),
-                    "zero_reduce_scatter_adam");
+                    where);
+}
+
+int zero_reduce_scatter_adam_dev(const uint16_t* const* rank_grads, const float* rank_weights,
+                                 int n_ranks, int64_t numel, int n_shards, float* const* master,
+                                 float* const* exp_avg, float* const* exp_avg_sq,
+                                 uint16_t* const* bf16_out, const float* const* grad_acc,
+                                 float* const* grad_out, const zero_adam_scalars* scalars_dev,
+                                 void* stream) {
+  Err e;
+  int st = check_reduce_scatter_adam_dev(rank_grads, rank_weights, n_ranks, numel, n_shards, master,
+                                         exp_avg, exp_avg_sq, bf16_out, grad_acc, grad_out, scalars_dev, e);
+  if (st) return fail(st, e.msg);
+  if (numel == 0) return ZERO_OK;
+  zero_adam_scalars unused;
+  memset(&unused, 0, sizeof unused);
+  return fused_common(rank_grads, rank_weights, n_ranks, numel, n_shards, master, exp_avg, exp_avg_sq,
+                      bf16_out, grad_acc, grad_out, unused, scalars_dev, stream, "zero_reduce_scatter_adam_dev");
+}
+
+int zero_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* rank_weights,
+                             int n_ranks, int64_t numel, int n_shards, float* const* master,
+                             float* const* exp_avg, float* const* exp_avg_sq,
+                             uint16_t* const* bf16_out, const float* const* grad_acc,
+                             float* const* grad_out, const zero_adam_hparams* hp, void* stream) {
+  Err e;
+  int st = check_reduce_scatter_adam(rank_grads, rank_weights, n_ranks, numel, n_shards, master,
+                                     exp_avg, exp_avg_sq, bf16_out, grad_acc, grad_out, hp, e);
+  if (st) return fail(st, e.msg);
+  if (numel == 0) return ZERO_OK;
+  zero_adam_scalars sc;
+  adam_scalars(hp, &sc, e);
+  return fused_common(rank_grads, rank_weights, n_ranks, numel, n_shards, master, exp_avg, exp_avg_sq,
+                      bf16_out, grad_acc, grad_out, sc, nullptr, stream, "zero_reduce_scatter_adam");
 }
 
 int zero_all_gather_layer(const void* const* shards, int n_shards, int64_t shard_bytes,

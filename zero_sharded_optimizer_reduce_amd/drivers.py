@@ -14,6 +14,8 @@ arithmetic step runs in the HIP kernels of libzero.
                     slide, note 原 N47)
 * OffloadStep       host-resident gradient shard through two device slots (blog,
                     section 分片放到 CPU：两个缓冲就够)
+* GraphedStep       a ShardedStep captured once into a HIP graph and replayed
+                    every step, the step's Adam scalars read from device memory
 """
 from __future__ import annotations
 
@@ -21,8 +23,9 @@ from typing import Optional, Sequence
 
 import torch
 
-from .api import (ZeroOffload, zero_adam_shard_step, zero_all_gather_layer, zero_reduce_scatter,
-                  zero_reduce_scatter_adam, zero_shard_layout)
+from .api import (ADAM_SCALARS_FLOATS, ZeroOffload, adam_scalars_tensor, zero_adam_shard_step,
+                  zero_adam_shard_step_dev, zero_all_gather_layer, zero_reduce_scatter, zero_reduce_scatter_adam,
+                  zero_reduce_scatter_adam_dev, zero_shard_layout)
 
 
 def _empty(n, dtype, device):
@@ -67,6 +70,58 @@ class ShardedStep:
         self.update(hp, stream)
         self.all_gather(stream)
         return self.view[: self.psi]
+
+
+class GraphedStep:
+    """A ShardedStep captured once into a HIP graph (torch.cuda.CUDAGraph) and
+    replayed at every step: reduce-scatter, the owners' updates, all-gather
+    (or the fused reduce + update storing the reduced shards, then the
+    all-gather).  The updates read the step's scalars from a device struct, so
+    each step() computes them on the host, copies them in on the replay
+    stream and replays; results are bit-identical to ShardedStep.step with the
+    same hyper-parameters.  The caller writes each step's contributions into
+    the captured rank_grads buffers; the rank weights are those of the capture.
+    Host staging for the scalars is a ring of pinned buffers, each reused only
+    after the copy that last read it has run."""
+
+    RING = 4
+
+    def __init__(self, st: ShardedStep, rank_grads, weights, fused: bool = False):
+        self.st = st
+        self.rank_grads = list(rank_grads)
+        dev = st.device
+        self.scalars = torch.zeros(ADAM_SCALARS_FLOATS, dtype=torch.float32, device=dev)
+        self._ring = [torch.empty(ADAM_SCALARS_FLOATS, dtype=torch.float32, pin_memory=True)
+                      for _ in range(self.RING)]
+        self._copied = [None] * self.RING
+        self._slot = 0
+        self.graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize(dev)
+        with torch.cuda.graph(self.graph):
+            if fused:
+                zero_reduce_scatter_adam_dev(self.rank_grads, weights, st.master, st.exp_avg, st.exp_avg_sq,
+                                             st.bf16, self.scalars, grad_out=st.grad)
+            else:
+                zero_reduce_scatter(self.rank_grads, weights, st.grad)
+                for k in range(st.n):
+                    zero_adam_shard_step_dev(st.master[k], st.exp_avg[k], st.exp_avg_sq[k], st.bf16[k],
+                                             st.grad[k], self.scalars)
+            zero_all_gather_layer(st.bf16, st.view)
+        torch.cuda.synchronize(dev)
+
+    def step(self, hp):
+        """One step on the current stream: this step's scalars, then the replay."""
+        i = self._slot
+        self._slot = (i + 1) % self.RING
+        if self._copied[i] is not None:
+            self._copied[i].synchronize()
+        adam_scalars_tensor(hp, out=self._ring[i])
+        self.scalars.copy_(self._ring[i], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self._copied[i] = ev
+        self.graph.replay()
+        return self.st.view[: self.st.psi]
 
 
 class BucketedOwnerStep:
