@@ -50,15 +50,16 @@ def _state(n, seed, special=False):
     return [f32_to_dev(x) for x in (p, m, v, g)]
 
 
-@pytest.mark.parametrize("n", [4096 * 3 + 4, 4096 + 3])
+@pytest.mark.parametrize("n,offset", [(4096 * 3 + 4, 0), (4096 + 3, 0), (4096 + 3, 1)])
 @pytest.mark.parametrize("wd", [0.0, 0.1])
 @pytest.mark.parametrize("scaled", [False, True])
-def test_update_with_device_scalars_equals_host_scalars(n, wd, scaled):
+def test_update_with_device_scalars_equals_host_scalars(n, offset, wd, scaled):
+    # offset 1: views one element into their buffers, so the element-wise kernels run
     hp = _hp(wd, 5)
-    a = _state(n, 11, special=True)
-    b = [x.clone() for x in a]
-    ba = torch.empty(n, dtype=torch.bfloat16, device="cuda")
-    bb = torch.empty_like(ba)
+    a = [x[offset:] for x in _state(n + offset, 11, special=True)]
+    b = [x.clone()[offset:] for x in _state(n + offset, 11, special=True)]
+    ba = torch.empty(n + offset, dtype=torch.bfloat16, device="cuda")[offset:]
+    bb = torch.empty(n + offset, dtype=torch.bfloat16, device="cuda")[offset:]
     scale = torch.tensor([0.37], device="cuda") if scaled else None
     if scaled:
         z.zero_adam_shard_step_scaled(a[0], a[1], a[2], ba, a[3], scale, hp)
@@ -66,6 +67,7 @@ def test_update_with_device_scalars_equals_host_scalars(n, wd, scaled):
         z.zero_adam_shard_step(a[0], a[1], a[2], ba, a[3], hp)
     dev = z.adam_scalars_tensor(hp).cuda()
     z.zero_adam_shard_step_dev(b[0], b[1], b[2], bb, b[3], dev, grad_scale=scale)
+    assert z.zero_last_path_vectorized() == (0 if offset else 1)
     torch.cuda.synchronize()
     for x, y, name in zip(a[:3] + [ba], b[:3] + [bb], ("master", "exp_avg", "exp_avg_sq", "bf16")):
         _same(x, y, f"{name} n={n} wd={wd} scaled={scaled}")
@@ -73,8 +75,9 @@ def test_update_with_device_scalars_equals_host_scalars(n, wd, scaled):
 
 @pytest.mark.parametrize("wd", [0.0, 0.1])
 @pytest.mark.parametrize("with_acc", [False, True])
-def test_fused_with_device_scalars_equals_host_scalars(wd, with_acc):
-    n, per = 4, 4096 + 4
+@pytest.mark.parametrize("per", [4096 + 4, 1001])
+def test_fused_with_device_scalars_equals_host_scalars(wd, with_acc, per):
+    n = 4
     grads = [S.bf16_normal(np.random.default_rng(r + 30), n * per, 1e-3) for r in range(n)]
     gd = [torch.from_numpy(g.view(np.int16)).cuda().view(torch.bfloat16) for g in grads]
     w = oracle.weights_from_counts([3, 5, 2, 7])
