@@ -118,3 +118,35 @@ def test_scalar_brute_force(psi, n):
         assert gs == float(gv[i])
         ps, ms, vs = _scalar_adam(float(p[i]), float(m[i]), float(v[i]), gs, sc)
         assert (ps, ms, vs) == (float(pv[i]), float(mv[i]), float(vv[i])), i
+
+
+def test_elastic_reshard_is_concat_then_split():
+    # the owners' state is a contiguous partition of one padded flat vector, so
+    # moving from N to N' owners is concatenation, re-padding and re-splitting:
+    # training N=4 for two steps, resharding to N'=2 and N'=8 and training a
+    # third step with N' ranks equals the replicated run with those ranks
+    psi = 3000
+    n0 = 4
+    _, pad0, _ = oracle.shard_layout([psi], n0)
+    g0, p, m, v, w0 = _setup(n0, psi, 70, counts=[5, 3, 5, 2])
+    flat = [oracle.flatten_pad([x], pad0) for x in (p, m, v)]
+    gpad = [oracle.flatten_pad([x], pad0) for x in g0]
+    owners = [[x[a:b] for a, b in (oracle.shard_bounds(pad0, n0, k) for k in range(n0))] for x in flat]
+    rep = [x.copy() for x in flat]
+    for t in (1, 2):
+        outs, _ = oracle.sharded_step(gpad, w0, owners[0], owners[1], owners[2], _sc(t, 0.1))
+        owners = [[o[1 + i] for o in outs] for i in range(3)]
+        _, rep[0], rep[1], rep[2], _ = oracle.ddp_step(gpad, w0, rep[0], rep[1], rep[2], _sc(t, 0.1))
+    for n1 in (2, 8):
+        _, pad1, _ = oracle.shard_layout([psi], n1)
+        state = [oracle.flatten_pad([np.concatenate(o)[:psi]], pad1) for o in owners]
+        g1, _, _, _, w1 = _setup(n1, psi, 80 + n1, counts=list(range(2, 2 + n1)))
+        g1p = [oracle.flatten_pad([x], pad1) for x in g1]
+        sl = [oracle.shard_bounds(pad1, n1, k) for k in range(n1)]
+        outs, view = oracle.sharded_step(g1p, w1, *[[x[a:b] for a, b in sl] for x in state], _sc(3, 0.1))
+        ref = oracle.ddp_step(g1p, w1, *[oracle.flatten_pad([x[:psi]], pad1) for x in rep], _sc(3, 0.1))
+        for i in range(3):
+            got = np.concatenate([o[1 + i] for o in outs])
+            assert np.array_equal(got[:psi].view(np.uint32), ref[1 + i][:psi].view(np.uint32)), (n1, i)
+            assert not got[psi:].any()          # padding stays zero (zero gradient, zero state)
+        assert np.array_equal(view[:psi], ref[4][:psi])
