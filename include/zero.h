@@ -310,6 +310,12 @@ const char* zero_last_error(void);
  * path (used by tests to cover both paths). */
 int zero_last_path_vectorized(void);
 
+/* 1 when the device entry points emit ROCTX ranges (one per call, named after
+ * the call): set ZERO_ROCTX=1 in the environment before the library's first
+ * call; ROCm's roctx library is then loaded at run time, and rocprofv3
+ * --marker-trace records the ranges.  0 otherwise (no cost). */
+int zero_tracing_enabled(void);
+
 #ifdef __cplusplus
 }
 #endif

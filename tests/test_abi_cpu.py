@@ -148,3 +148,22 @@ def test_fused_validation_alias_rules(libzero):
     # a rank buffer equal to grad_out == grad_acc: rejected
     assert L.zero_reduce_scatter_adam(_pp(0x500000), _w(1), 1, 1024, 1, P, M, V, B, acc, acc, C.byref(hp),
                                       None) == -1
+
+
+def test_roctx_tracing_switch():
+    # ZERO_ROCTX=1 loads ROCm's roctx library at the first use; without it the
+    # library emits nothing.  Each case runs in a fresh interpreter (no GPU use).
+    import os
+    import subprocess
+    import sys
+    code = ("import ctypes, sys; sys.path.insert(0, %r); "
+            "from zero_sharded_optimizer_reduce_amd import _lib; "
+            "print(_lib.load().zero_tracing_enabled())") % ROOT
+    for flag, want in (("1", "1"), ("0", "0"), (None, "0")):
+        env = dict(os.environ)
+        env.pop("ZERO_ROCTX", None)
+        if flag is not None:
+            env["ZERO_ROCTX"] = flag
+        r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=120)
+        assert r.returncode == 0, r.stderr
+        assert r.stdout.strip() == want, (flag, r.stdout)

@@ -56,6 +56,7 @@ SIGNATURES = {
     "zero_status_string": (C.c_char_p, [C.c_int]),
     "zero_last_error": (C.c_char_p, []),
     "zero_last_path_vectorized": (C.c_int, []),
+    "zero_tracing_enabled": (C.c_int, []),
 }
 
 _LIB = None

@@ -92,4 +92,18 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t value, int64_t n, hipStream_t s
 // Gather path selector: 16-byte, 4-byte or 1-byte units.
 enum { GATHER_V16 = 0, GATHER_U32 = 1, GATHER_U8 = 2 };
 
+// A ROCTX range for the lifetime of the object when tracing is on
+// (ZERO_ROCTX=1); a no-op otherwise.
+class TraceRange {
+ public:
+  explicit TraceRange(const char* name);
+  ~TraceRange();
+  TraceRange(const TraceRange&) = delete;
+  TraceRange& operator=(const TraceRange&) = delete;
+
+ private:
+  bool on_;
+};
+int tracing_enabled();
+
 }  // namespace zero

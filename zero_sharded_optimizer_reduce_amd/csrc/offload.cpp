@@ -174,6 +174,7 @@ int zero_offload_stream(zero_offload* h, int op, int64_t chunk, int micro_batch,
                         const float* rank_weights, float* master, float* exp_avg,
                         float* exp_avg_sq, uint16_t* bf16_out, const zero_adam_hparams* hp,
                         void* compute_stream) {
+  TraceRange tr("zero_offload_stream");
   if (!h) return fail(ZERO_ERR_ARG, "offload_stream: NULL handle");
   if (op != ZERO_OFFLOAD_REDUCE && op != ZERO_OFFLOAD_ADAM && op != ZERO_OFFLOAD_REDUCE_ADAM)
     return fail(ZERO_ERR_ARG, "offload_stream: unknown op");

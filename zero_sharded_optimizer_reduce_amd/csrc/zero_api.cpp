@@ -1,9 +1,11 @@
 // C ABI entry points of libzero (declared in include/zero.h): validate on the
 // host, pick the 16-byte or element-wise kernel path, launch on the caller's
 // stream.  No call allocates, frees or synchronises.
+#include <dlfcn.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "kernels.h"
@@ -27,6 +29,42 @@ int hip_status(hipError_t err, const char* where) {
 
 void set_path(bool vec) { g_last_vec = vec ? 1 : 0; }
 
+// Optional ROCTX ranges around the device entry points (ZERO_ROCTX=1 in the
+// environment when the library is first used): ROCm's roctx library is
+// loaded at run time, so nothing is linked or called when tracing is off.
+// rocprofv3 --marker-trace then shows one range per call on the host
+// timeline.
+namespace {
+struct Roctx {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+
+const Roctx& roctx() {
+  static const Roctx r = [] {
+    Roctx x;
+    const char* e = std::getenv("ZERO_ROCTX");
+    if (!e || std::atoi(e) == 0) return x;
+    void* h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+    if (!h) return x;
+    x.push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+    x.pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+    if (!x.push || !x.pop) x = Roctx();
+    return x;
+  }();
+  return r;
+}
+}  // namespace
+
+TraceRange::TraceRange(const char* name) : on_(roctx().push != nullptr) {
+  if (on_) roctx().push(name);
+}
+TraceRange::~TraceRange() {
+  if (on_) roctx().pop();
+}
+
+int tracing_enabled() { return roctx().push != nullptr ? 1 : 0; }
+
 }  // namespace zero
 
 using namespace zero;
@@ -48,6 +86,8 @@ const char* zero_status_string(int status) {
 const char* zero_last_error(void) { return g_last_error; }
 
 int zero_last_path_vectorized(void) { return g_last_vec; }
+
+int zero_tracing_enabled(void) { return tracing_enabled(); }
 
 int zero_adam_scalars_compute(const zero_adam_hparams* hp, zero_adam_scalars* out) {
   Err e;
@@ -71,6 +111,7 @@ int zero_shard_layout(const int64_t* numels, int n_tensors, int n_shards, int64_
 int zero_reduce_scatter(const uint16_t* const* rank_grads, const float* rank_weights, int n_ranks,
                         int64_t numel, float* const* shards_out, int n_shards, int accumulate,
                         void* stream) {
+  TraceRange tr("zero_reduce_scatter");
   Err e;
   int st = check_reduce_scatter(reinterpret_cast<const void* const*>(rank_grads), rank_weights,
                                 n_ranks, numel, shards_out, n_shards, accumulate, e);
@@ -126,6 +167,7 @@ static int adam_common(float* master, float* exp_avg, float* exp_avg_sq, uint16_
 int zero_reduce_scatter_f32(const float* const* rank_grads, const float* rank_weights, int n_ranks,
                             int64_t numel, float* const* shards_out, int n_shards, int accumulate,
                             void* stream) {
+  TraceRange tr("zero_reduce_scatter_f32");
   Err e;
   int st = check_reduce_scatter(reinterpret_cast<const void* const*>(rank_grads), rank_weights, n_ranks,
                                 numel, shards_out, n_shards, accumulate, e, 4);
@@ -153,6 +195,7 @@ int zero_reduce_scatter_f32(const float* const* rank_grads, const float* rank_we
 
 int zero_adam_shard_step(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* bf16_out,
                          const float* grad, int64_t n, const zero_adam_hparams* hp, void* stream) {
+  TraceRange tr("zero_adam_shard_step");
   return adam_common(master, exp_avg, exp_avg_sq, bf16_out, grad, nullptr, n, hp, stream,
                      "zero_adam_shard_step");
 }
@@ -160,6 +203,7 @@ int zero_adam_shard_step(float* master, float* exp_avg, float* exp_avg_sq, uint1
 int zero_adam_shard_step_scaled(float* master, float* exp_avg, float* exp_avg_sq,
                                 uint16_t* bf16_out, const float* grad, const float* grad_scale,
                                 int64_t n, const zero_adam_hparams* hp, void* stream) {
+  TraceRange tr("zero_adam_shard_step_scaled");
   if (!grad_scale && n > 0) return fail(ZERO_ERR_ARG, "adam_scaled: NULL grad_scale");
   return adam_common(master, exp_avg, exp_avg_sq, bf16_out, grad, grad_scale, n, hp, stream,
                      "zero_adam_shard_step_scaled");
@@ -168,6 +212,7 @@ int zero_adam_shard_step_scaled(float* master, float* exp_avg, float* exp_avg_sq
 int zero_grad_norm_sq(const float* const* shards, int n_shards, int64_t shard_numel,
                       double* workspace, int64_t workspace_len, double* norm_sq_out,
                       float max_norm, float* clip_coef_out, void* stream) {
+  TraceRange tr("zero_grad_norm_sq");
   Err e;
   int st = check_grad_norm(shards, n_shards, shard_numel, workspace, workspace_len, norm_sq_out,
                            max_norm, clip_coef_out, e);
@@ -192,6 +237,7 @@ int zero_grad_norm_sq(const float* const* shards, int n_shards, int64_t shard_nu
 int zero_adam_shard_step_dev(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* bf16_out,
                              const float* grad, const float* grad_scale, int64_t n,
                              const zero_adam_scalars* scalars_dev, void* stream) {
+  TraceRange tr("zero_adam_shard_step_dev");
   Err e;
   int st = check_adam_dev(master, exp_avg, exp_avg_sq, bf16_out, grad, n, scalars_dev, e);
   if (st) return fail(st, e.msg);
@@ -254,6 +300,7 @@ int zero_reduce_scatter_adam_dev(const uint16_t* const* rank_grads, const float*
                                  uint16_t* const* bf16_out, const float* const* grad_acc,
                                  float* const* grad_out, const zero_adam_scalars* scalars_dev,
                                  void* stream) {
+  TraceRange tr("zero_reduce_scatter_adam_dev");
   Err e;
   int st = check_reduce_scatter_adam_dev(rank_grads, rank_weights, n_ranks, numel, n_shards, master,
                                          exp_avg, exp_avg_sq, bf16_out, grad_acc, grad_out, scalars_dev, e);
@@ -270,6 +317,7 @@ int zero_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* ran
                              float* const* exp_avg, float* const* exp_avg_sq,
                              uint16_t* const* bf16_out, const float* const* grad_acc,
                              float* const* grad_out, const zero_adam_hparams* hp, void* stream) {
+  TraceRange tr("zero_reduce_scatter_adam");
   Err e;
   int st = check_reduce_scatter_adam(rank_grads, rank_weights, n_ranks, numel, n_shards, master,
                                      exp_avg, exp_avg_sq, bf16_out, grad_acc, grad_out, hp, e);
@@ -283,6 +331,7 @@ int zero_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* ran
 
 int zero_all_gather_layer(const void* const* shards, int n_shards, int64_t shard_bytes,
                           void* full_view, void* stream) {
+  TraceRange tr("zero_all_gather_layer");
   Err e;
   int st = check_all_gather(shards, n_shards, shard_bytes, full_view, e);
   if (st) return fail(st, e.msg);
