@@ -74,7 +74,11 @@ def shard_layout(numels: Iterable[int], n_shards: int, align: int = SHARD_ALIGN)
 
 
 def flatten_pad(tensors: Sequence[np.ndarray], psi_pad: int) -> np.ndarray:
-    """Concatenate the unit's tensors in the stated order, zero-padded to psi_pad."""
+    """Concatenate the unit's tensors in the stated order, zero-padded to psi_pad.
+
+    The shards are slices of the flattened parameters, not layers (slide, note
+    原 N46); the zero padding that makes the N slices equal is the reading
+    taken where the pages are silent."""
     flat = np.concatenate([np.asarray(t).reshape(-1) for t in tensors]) if tensors else np.zeros(0)
     assert flat.size <= psi_pad
     out = np.zeros(psi_pad, dtype=flat.dtype)
@@ -83,7 +87,9 @@ def flatten_pad(tensors: Sequence[np.ndarray], psi_pad: int) -> np.ndarray:
 
 
 def shard_bounds(psi_pad: int, n_shards: int, k: int):
-    """Owner k's contiguous slice [k*S, (k+1)*S) of the padded flat vector."""
+    """Owner k's contiguous slice [k*S, (k+1)*S) of the padded flat vector: each
+    of the N devices keeps 1/N of the state (blog, section 三级分片; slide,
+    note 原 N46, shards theta_0..theta_{N-1})."""
     assert psi_pad % n_shards == 0 and 0 <= k < n_shards
     s = psi_pad // n_shards
     return k * s, (k + 1) * s
@@ -116,7 +122,9 @@ def weights_from_counts(counts: Sequence[int]) -> np.ndarray:
 # the top 7 fraction bits of binary32)
 # ---------------------------------------------------------------------------
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
-    """Exact widening: a bf16 bit pattern is the high half of a binary32."""
+    """Exact widening: a bf16 bit pattern is the high half of a binary32.  The
+    working weights and gradients are 2-byte BF16 next to the 4-byte FP32
+    master and moments (blog, section 每个参数 16 字节)."""
     bits = np.asarray(bits)
     assert bits.dtype == U16, bits.dtype
     return (bits.astype(U32) << U32(16)).view(F32)
@@ -124,6 +132,10 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
 
 def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
     """Round binary32 values to the nearest bfloat16, ties to even mantissa.
+
+    The BF16 working weight is derived from the FP32 master (blog, section
+    每个参数 16 字节); the pages do not state a rounding mode, and
+    round-to-nearest-even is the reading taken.
 
     Written from the definition: the two bf16 neighbours of |x| are the
     truncation `lo` and the next bf16 magnitude `hi` (the next bit pattern;
@@ -204,11 +216,16 @@ def reduce_owner_shard(rank_grads: Sequence[np.ndarray], weights: np.ndarray,
 
 
 def reduce_scatter(rank_grads, weights, n_shards: int):
+    """Every owner's reduced shard: contributions combined element by element,
+    each participant keeping its own fragment (essay, section ZeRO-3 的一次完整
+    计算)."""
     return [reduce_owner_shard(rank_grads, weights, n_shards, k) for k in range(n_shards)]
 
 
 def reduce_accumulate(acc: np.ndarray, rank_grads, weights) -> np.ndarray:
-    """Accumulate mode: acc + (sum_r w_r x_r), the reduction formed first."""
+    """Accumulate mode: acc + (sum_r w_r x_r), the reduction formed first: a
+    chunk reduced across the data ranks is added onto the accumulated shard
+    (blog, section 分片放到 CPU：两个缓冲就够)."""
     _chk32(acc)
     return _chk32(acc + reduce_full(rank_grads, weights))
 
@@ -217,7 +234,9 @@ def reduce_accumulate(acc: np.ndarray, rank_grads, weights) -> np.ndarray:
 # a4/a5: mixed-precision Adam owner update, BF16 working-weight pack
 # ---------------------------------------------------------------------------
 def adam_scalars(lr, beta1, beta2, eps, weight_decay, step: int) -> dict:
-    """Per-step scalars, formed once on the host.
+    """Per-step scalars, formed once on the host.  The pages name only Adam's
+    two history statistics (essay, section 从持久状态开始记账); the bias
+    corrections 1 - beta_i**t are those of Kingma & Ba's Algorithm 1.
 
     beta_i and the other hyper-parameters are rounded to float32; 1 - beta_i is
     a float32 subtraction (exact, since beta_i lies in [1/2, 1]); the bias
@@ -334,7 +353,8 @@ def offload_accumulate(per_micro_batch_grads: Sequence[Sequence[np.ndarray]], we
 # ---------------------------------------------------------------------------
 def grad_norm_sq(shards: Sequence[np.ndarray]) -> float:
     """Sum of squares of every element of every shard, in float64 (the squares
-    of binary32 values are exact in binary64)."""
+    of binary32 values are exact in binary64).  Gradient clipping is not
+    described by the pages; this is the plain reading of a global norm."""
     total = 0.0
     for x in shards:
         x64 = _chk32(np.asarray(x)).astype(np.float64)
@@ -343,13 +363,15 @@ def grad_norm_sq(shards: Sequence[np.ndarray]) -> float:
 
 
 def clip_coefficient(norm_sq: float, max_norm: float) -> np.float32:
-    """float32(min(1, max_norm / (sqrt(norm_sq) + 1e-6))), evaluated in float64."""
+    """float32(min(1, max_norm / (sqrt(norm_sq) + 1e-6))), evaluated in float64
+    (not described by the pages: the plain reading of norm clipping)."""
     c = float(np.float32(max_norm)) / (math.sqrt(norm_sq) + 1e-6)
     return np.float32(min(1.0, c))
 
 
 def scale_grad(g: np.ndarray, coef: np.float32) -> np.ndarray:
-    """The clipped gradient: one binary32 multiply per element."""
+    """The clipped gradient: one binary32 multiply per element (not described by
+    the pages: the plain reading of norm clipping)."""
     assert type(coef) is np.float32
     return _chk32(_chk32(np.asarray(g)) * coef)
 
@@ -362,7 +384,8 @@ WEIGHT_B, GRAD_B, MASTER_B, MOMENT_B = 2, 2, 4, 4
 
 
 def ledger_bytes_per_param(stage: int, n: int, moments: int = 2, grad_bytes: int = GRAD_B) -> Fraction:
-    """Persistent bytes per parameter per device.
+    """Persistent bytes per parameter per device (blog, section 每个参数 16 字节
+    and the table of section 三级分片; slide, notes 原 N46 and 原 N47).
 
     stage 0 is replicated DP; stage 1 shards the optimizer state (master and
     moments); stage 2 also shards the gradient; stage 3 also shards the
@@ -382,5 +405,6 @@ def ledger_bytes_per_param(stage: int, n: int, moments: int = 2, grad_bytes: int
 
 
 def ledger_gb(stage: int, n: int, psi: int, **kw) -> Fraction:
-    """Persistent state per device in GB (1 GB = 10**9 bytes)."""
+    """Persistent state per device in GB (1 GB = 10**9 bytes), as the slide's
+    note 原 N47 prints it for an 8B model on 4 cards."""
     return ledger_bytes_per_param(stage, n, **kw) * psi / 10 ** 9
