@@ -209,8 +209,11 @@ int zero_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* ran
                              float* const* grad_out, const zero_adam_hparams* hp, void* stream);
 
 /* Graph-capturable forms of the owner update and of the fused call: the same
- * arithmetic, with the step's scalars read from device memory when the kernel
- * runs instead of being passed by value at the call.  A caller that captures
+ * operations ([slide] note 原 N48: the owner updates its master weights and
+ * m/v with the combined gradient; [blog] 三级分片, ZeRO-1: the step between
+ * the reduce-scatter and the all-gather) and the same arithmetic, with the
+ * step's scalars read from device memory when the kernel runs instead of
+ * being passed by value at the call.  A caller that captures
  * a step into a HIP graph writes each step's scalars (zero_adam_scalars_compute
  * on the host, then a copy to the device struct on the replay stream) before
  * each replay; the captured launches then apply that step's bias corrections.
