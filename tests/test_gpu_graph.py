@@ -147,3 +147,32 @@ def test_device_scalar_arguments_are_validated():
     g[:z.ADAM_SCALARS_FLOATS] = dev
     z.zero_adam_shard_step_dev(p, m, v, b, g, g[:z.ADAM_SCALARS_FLOATS])
     torch.cuda.synchronize()
+
+
+def test_graph_replays_equal_eager_steps_on_the_7b_layer():
+    # the configuration the benchmark's graph variant times, at full size
+    from synthetic.workloads import LAYER_7B as wl
+    n = wl.n_ranks
+    numels = S.unit_numels(S.workloads.layer_7b_tensors())
+    gen = S.DeviceGen(wl.seed + 60)
+    eager, graphed = ShardedStep(numels, n), ShardedStep(numels, n)
+    master0 = gen.normal_(torch.empty(eager.psi_pad, device="cuda"), wl.master_sigma, 0)
+    eager.load_master(master0)
+    graphed.load_master(master0)
+    del master0
+    w = z.zero_rank_weights(wl.extra["token_counts"], n)
+    grads = [torch.empty(eager.psi_pad, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    tmp = torch.empty(eager.psi_pad, device="cuda")
+    g = GraphedStep(graphed, grads, w)
+    for t in range(1, 4):
+        print(f"7B layer graph replay, step {t}", flush=True)
+        for r in range(n):
+            gen.bf16_normal_(grads[r], wl.grad_sigma, t, r, tmp=tmp)
+        hp = wl.hparams(step=t)
+        eager.step(grads, w, hp)
+        g.step(hp)
+        torch.cuda.synchronize()
+        for name in ("master", "exp_avg", "exp_avg_sq", "bf16", "grad"):
+            for k in range(n):
+                _same(getattr(eager, name)[k], getattr(graphed, name)[k], f"step {t} {name}[{k}]")
+        _same(eager.view, graphed.view, f"step {t} view")
