@@ -52,6 +52,48 @@ __device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_lo
 template <typename T>
 __device__ __forceinline__ void st_nt(T v, T* p) { __builtin_nontemporal_store(v, p); }
 
+// Streamed output stores with a cache policy the compiler's builtin cannot
+// set.  With SC1 a workgroup writes its tile through a buffer descriptor based
+// at the tile's first element (workgroup-uniform, so the descriptor lives in
+// scalar registers and every lane offset is below 4 KiB), with the store bits
+// nt and sc1 (device scope); without it the plain non-temporal store is used.
+// Same-box A/B on MI355X: with sc1 the update, the fused kernel (without the
+// gradient output), the accumulate-mode reduce and the gather ran 1.4-3.6%
+// faster; the plain reduce, the FP32-contribution reduce and the fused kernel
+// storing the gradient ran 0.4-1.8% slower, so they keep the plain store.
+// The buffer forms are compiler intrinsics (not inline assembly), so the
+// compiler schedules them and resolves their register hazards.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+constexpr int kRawBufferFlags = 0x00020000;   // dword 3 of a raw buffer descriptor: 32-bit data format
+constexpr int kStoreNtSc1 = 2 | 16;           // cache-policy operand: nt | sc1
+
+template <typename T, bool SC1>
+struct TileOut {
+  T* global;                  // the tile's first element
+  __amdgpu_buffer_rsrc_t rsrc;
+  __device__ __forceinline__ TileOut(T* base, int64_t count) : global(base) {
+    if constexpr (SC1)
+      rsrc = __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(count * static_cast<int64_t>(sizeof(T))),
+                                               kRawBufferFlags);
+  }
+  // element j of the tile (0 <= j < count)
+  __device__ __forceinline__ void store(T v, int j) const {
+    if constexpr (!SC1) {
+      __builtin_nontemporal_store(v, global + j);
+    } else if constexpr (sizeof(T) == 16) {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), rsrc, j * 16, 0, kStoreNtSc1);
+    } else if constexpr (sizeof(T) == 8) {
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, v), rsrc, j * 8, 0, kStoreNtSc1);
+    } else {
+      __builtin_nontemporal_store(v, global + j);
+    }
+  }
+};
+
+// Elements of the tile that starts `left` elements before the end of an array.
+__device__ __forceinline__ int64_t tile_len(int64_t left, int bs) { return left < bs ? left : bs; }
+
 // ------------------------------------------------------------ reduce-scatter
 // Owner k, element i (global index j = k*shard + i):
 //   red = w_0*x_0[j]; red = red + w_r*x_r[j] for r = 1..N-1 (rank order),
@@ -62,8 +104,12 @@ __device__ __forceinline__ void st_nt(T v, T* p) { __builtin_nontemporal_store(v
 // Vector path: each lane reduces 4 consecutive elements: one 8-byte BF16 load
 // per rank, one 16-byte FP32 store, so every load and store instruction of a
 // wave covers one contiguous span (16-byte loads with two strided 16-byte
-// stores measured 5% slower: the stores then cover half lines).  U vectors
-// per lane keep N*U loads in flight before the first use.
+// stores measured 5% slower: the stores then cover half lines).  A workgroup
+// takes one tile of BS vectors per loop iteration; lanes past the end of the
+// shard skip the whole body, so a lane's N contribution loads sit in one
+// basic block and are all in flight before the first wait (a guard per load
+// made the compiler wait for each load before issuing the next: 10-16%
+// slower).
 
 // The 4 reduced values of one lane; x[r] holds rank r's 4 BF16 values.
 template <int NMAX>
@@ -128,7 +174,7 @@ __global__ __launch_bounds__(kBlock) void rs_f32_scalar_kernel(RsParams p) {
   }
 }
 
-template <int N, bool ACC, int U, int BS>
+template <int N, bool ACC, int BS>
 __global__ __launch_bounds__(BS) void rs_vec_kernel(RsParams p) {
   constexpr int NMAX = N > 0 ? N : ZERO_MAX_RANKS;
   const int n = N > 0 ? N : p.n_ranks;
@@ -136,24 +182,23 @@ __global__ __launch_bounds__(BS) void rs_vec_kernel(RsParams p) {
   const int64_t nvec = p.shard >> 2;
   const int64_t off = static_cast<int64_t>(k) * nvec;
   f32x4* __restrict__ out = reinterpret_cast<f32x4*>(p.out[k]);
-  const int64_t step = static_cast<int64_t>(gridDim.x) * BS * U;
-  for (int64_t base = static_cast<int64_t>(blockIdx.x) * BS * U + threadIdx.x; base < nvec;
-       base += step) {
-    u32x2 x[U][NMAX];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = base + u * BS;
+  const int64_t step = static_cast<int64_t>(gridDim.x) * BS;
+  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * BS; tile < nvec; tile += step) {
+    const int64_t i = tile + threadIdx.x;
+    if (i < nvec) {
+      const TileOut<f32x4, ACC> o(out + tile, tile_len(nvec - tile, BS));
+      u32x2 x[NMAX];
 #pragma unroll
       for (int r = 0; r < NMAX; ++r)
-        if (r < n && i < nvec) x[u][r] = ld_nt(reinterpret_cast<const u32x2*>(p.g[r]) + off + i);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = base + u * BS;
-      if (i >= nvec) break;
-      f32x4 a = reduce4<NMAX>(x[u], n, p.w);
-      if (ACC) a = out[i] + a;
-      st_nt(a, out + i);
+        if (r < n) x[r] = ld_nt(reinterpret_cast<const u32x2*>(p.g[r]) + off + i);
+      f32x4 prev;
+      if (ACC) prev = out[i];
+      // Keep the scheduler from starting the conversion of rank 0's values
+      // (and waiting for them) before the last load is issued.
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 a = reduce4<NMAX>(x, n, p.w);
+      if (ACC) a = prev + a;
+      o.store(a, threadIdx.x);
     }
   }
 }
@@ -204,10 +249,11 @@ __device__ __forceinline__ void adam_elem(float& p, float& m, float& v, float g,
 }
 
 // One pass: read g, p, m, v (16 B/param), write p, m, v and the BF16 working
-// weight (14 B/param).  Vector path: 4 elements per 16-byte access, U vectors
-// per lane per iteration; the n % 4 tail goes element-wise.  SC: the gradient
+// weight (14 B/param).  Vector path: 4 elements per 16-byte access, one
+// tile of BS vectors per workgroup and loop iteration, lanes past the end
+// skipping the whole body; the n % 4 tail goes element-wise.  SC: the gradient
 // is first multiplied by the device scalar *gscale (the clip coefficient).
-template <int WD, bool SC, int U, int BS>
+template <int WD, bool SC, int BS>
 __global__ __launch_bounds__(BS) void adam_vec_kernel(AdamParams a) {
   const zero_adam_scalars s = step_scalars<WD>(a.s, a.sdev);
   const int64_t nvec = a.n >> 2;
@@ -217,35 +263,26 @@ __global__ __launch_bounds__(BS) void adam_vec_kernel(AdamParams a) {
   const f32x4* __restrict__ G = reinterpret_cast<const f32x4*>(a.g);
   u32x2* __restrict__ B = reinterpret_cast<u32x2*>(a.b);
   const float c = SC ? *a.gscale : 1.0f;
-  const int64_t step = static_cast<int64_t>(gridDim.x) * BS * U;
-  for (int64_t base = static_cast<int64_t>(blockIdx.x) * BS * U + threadIdx.x; base < nvec;
-       base += step) {
-    f32x4 g[U], p[U], m[U], v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = base + u * BS;
-      if (i < nvec) {
-        g[u] = ld_nt(G + i);
-        p[u] = ld_nt(P + i);
-        m[u] = ld_nt(M + i);
-        v[u] = ld_nt(V + i);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = base + u * BS;
-      if (i >= nvec) break;
-      if (SC) g[u] = g[u] * c;
-      float pe[4] = {p[u].x, p[u].y, p[u].z, p[u].w};
-      float me[4] = {m[u].x, m[u].y, m[u].z, m[u].w};
-      float ve[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-      const float ge[4] = {g[u].x, g[u].y, g[u].z, g[u].w};
+  const int64_t step = static_cast<int64_t>(gridDim.x) * BS;
+  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * BS; tile < nvec; tile += step) {
+    const int64_t i = tile + threadIdx.x;
+    if (i < nvec) {
+      const int64_t len = tile_len(nvec - tile, BS);
+      const TileOut<f32x4, true> oP(P + tile, len), oM(M + tile, len), oV(V + tile, len);
+      const TileOut<u32x2, true> oB(B + tile, len);
+      f32x4 g = ld_nt(G + i);
+      const f32x4 pv = ld_nt(P + i), mv = ld_nt(M + i), vv = ld_nt(V + i);
+      if (SC) g = g * c;
+      float pe[4] = {pv.x, pv.y, pv.z, pv.w};
+      float me[4] = {mv.x, mv.y, mv.z, mv.w};
+      float ve[4] = {vv.x, vv.y, vv.z, vv.w};
+      const float ge[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) adam_elem<WD>(pe[e], me[e], ve[e], ge[e], s);
-      st_nt(f32x4{pe[0], pe[1], pe[2], pe[3]}, P + i);
-      st_nt(f32x4{me[0], me[1], me[2], me[3]}, M + i);
-      st_nt(f32x4{ve[0], ve[1], ve[2], ve[3]}, V + i);
-      st_nt(u32x2{to_bf16x2(pe[0], pe[1]), to_bf16x2(pe[2], pe[3])}, B + i);
+      oP.store(f32x4{pe[0], pe[1], pe[2], pe[3]}, threadIdx.x);
+      oM.store(f32x4{me[0], me[1], me[2], me[3]}, threadIdx.x);
+      oV.store(f32x4{ve[0], ve[1], ve[2], ve[3]}, threadIdx.x);
+      oB.store(u32x2{to_bf16x2(pe[0], pe[1]), to_bf16x2(pe[2], pe[3])}, threadIdx.x);
     }
   }
   const int64_t tail = a.n - (nvec << 2);
@@ -360,7 +397,7 @@ __global__ __launch_bounds__(kBlock) void norm_final_kernel(NormParams p) {
 // micro-batch of an accumulation updates directly).  Bytes per parameter
 // (N=4): 8 (contributions) + 12 (state) read, 12 (state) + 2 (BF16) written
 // = 34, against 12 + 30 = 42 for the two kernels.
-template <int N, int WD, bool WG, bool ACC, int U, int BS>
+template <int N, int WD, bool WG, bool ACC, int BS>
 __global__ __launch_bounds__(BS) void fused_vec_kernel(FusedParams p) {
   const zero_adam_scalars s = step_scalars<WD>(p.s, p.sdev);
   constexpr int NMAX = N > 0 ? N : ZERO_MAX_RANKS;
@@ -374,41 +411,31 @@ __global__ __launch_bounds__(BS) void fused_vec_kernel(FusedParams p) {
   u32x2* __restrict__ B = reinterpret_cast<u32x2*>(p.b[k]);
   f32x4* __restrict__ GO = reinterpret_cast<f32x4*>(p.gout[k]);
   const f32x4* __restrict__ GA = reinterpret_cast<const f32x4*>(p.gacc[k]);
-  const int64_t step = static_cast<int64_t>(gridDim.x) * BS * U;
-  for (int64_t base = static_cast<int64_t>(blockIdx.x) * BS * U + threadIdx.x; base < nvec;
-       base += step) {
-    u32x2 x[U][NMAX];
-    f32x4 pv[U], mv[U], vv[U], av[U];
+  const int64_t step = static_cast<int64_t>(gridDim.x) * BS;
+  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * BS; tile < nvec; tile += step) {
+    const int64_t i = tile + threadIdx.x;
+    if (i < nvec) {
+      const int64_t len = tile_len(nvec - tile, BS);
+      const TileOut<f32x4, !WG> oP(P + tile, len), oM(M + tile, len), oV(V + tile, len);
+      const TileOut<u32x2, !WG> oB(B + tile, len);
+      u32x2 x[NMAX];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = base + u * BS;
-      if (i < nvec) {
-#pragma unroll
-        for (int r = 0; r < NMAX; ++r)
-          if (r < n) x[u][r] = ld_nt(reinterpret_cast<const u32x2*>(p.g[r]) + off + i);
-        pv[u] = ld_nt(P + i);
-        mv[u] = ld_nt(M + i);
-        vv[u] = ld_nt(V + i);
-        if (ACC) av[u] = ld_nt(GA + i);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = base + u * BS;
-      if (i >= nvec) break;
-      f32x4 g = reduce4<NMAX>(x[u], n, p.w);
-      if (ACC) g = av[u] + g;
+      for (int r = 0; r < NMAX; ++r)
+        if (r < n) x[r] = ld_nt(reinterpret_cast<const u32x2*>(p.g[r]) + off + i);
+      const f32x4 pv = ld_nt(P + i), mv = ld_nt(M + i), vv = ld_nt(V + i);
+      f32x4 g = reduce4<NMAX>(x, n, p.w);
+      if (ACC) g = ld_nt(GA + i) + g;
       if (WG) st_nt(g, GO + i);
-      float pe[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
-      float me[4] = {mv[u].x, mv[u].y, mv[u].z, mv[u].w};
-      float ve[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+      float pe[4] = {pv.x, pv.y, pv.z, pv.w};
+      float me[4] = {mv.x, mv.y, mv.z, mv.w};
+      float ve[4] = {vv.x, vv.y, vv.z, vv.w};
       const float ge[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) adam_elem<WD>(pe[e], me[e], ve[e], ge[e], s);
-      st_nt(f32x4{pe[0], pe[1], pe[2], pe[3]}, P + i);
-      st_nt(f32x4{me[0], me[1], me[2], me[3]}, M + i);
-      st_nt(f32x4{ve[0], ve[1], ve[2], ve[3]}, V + i);
-      st_nt(u32x2{to_bf16x2(pe[0], pe[1]), to_bf16x2(pe[2], pe[3])}, B + i);
+      oP.store(f32x4{pe[0], pe[1], pe[2], pe[3]}, threadIdx.x);
+      oM.store(f32x4{me[0], me[1], me[2], me[3]}, threadIdx.x);
+      oV.store(f32x4{ve[0], ve[1], ve[2], ve[3]}, threadIdx.x);
+      oB.store(u32x2{to_bf16x2(pe[0], pe[1]), to_bf16x2(pe[2], pe[3])}, threadIdx.x);
     }
   }
 }
@@ -436,22 +463,20 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(FusedParams p) {
 // ---------------------------------------------------------------- all-gather
 // The full view is the owners' shards concatenated in owner order (essay,
 // section ZeRO-3 的一次完整计算; slide, note 原 N47).  Owner k = blockIdx.y.
-template <typename T, int U, int BS>
+template <typename T, int BS>
 __global__ __launch_bounds__(BS) void gather_kernel(GatherParams p) {
   const int k = blockIdx.y;
   const int64_t n = p.shard_bytes / static_cast<int64_t>(sizeof(T));
   const T* __restrict__ src = reinterpret_cast<const T*>(p.src[k]);
   T* __restrict__ dst = reinterpret_cast<T*>(static_cast<char*>(p.dst) + k * p.shard_bytes);
-  const int64_t step = static_cast<int64_t>(gridDim.x) * BS * U;
-  for (int64_t base = static_cast<int64_t>(blockIdx.x) * BS * U + threadIdx.x; base < n;
-       base += step) {
-    T x[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (base + u * BS < n) x[u] = ld_nt(src + base + u * BS);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (base + u * BS < n) st_nt(x[u], dst + base + u * BS);
+  const int64_t step = static_cast<int64_t>(gridDim.x) * BS;
+  constexpr bool kSc1 = sizeof(T) == 16;   // the 16-byte path stores with nt | sc1
+  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * BS; tile < n; tile += step) {
+    const int64_t i = tile + threadIdx.x;
+    if (i < n) {
+      const TileOut<T, kSc1> o(dst + tile, tile_len(n - tile, BS));
+      o.store(ld_nt(src + i), threadIdx.x);
+    }
   }
 }
 
@@ -494,10 +519,10 @@ int device_cus() {
   return cache[dev];
 }
 
-// Blocks along x for `units` work items per owner, each block covering
-// bs*u of them per loop iteration.
-unsigned grid_x(int64_t units, int u, int n_y, int bs = kBlock) {
-  const int64_t per_iter = static_cast<int64_t>(bs) * u;
+// Blocks along x for `units` work items per owner, each block covering bs of
+// them per loop iteration.
+unsigned grid_x(int64_t units, int n_y, int bs = kBlock) {
+  const int64_t per_iter = bs;
   int64_t need = (units + per_iter - 1) / per_iter;
   int64_t cap = kMaxGridX;
   if (blocks_per_cu() > 0) cap = static_cast<int64_t>(device_cus()) * blocks_per_cu() / (n_y > 0 ? n_y : 1);
@@ -533,13 +558,6 @@ constexpr unsigned kRsAccResidencyLds = 8 * 1024;    // 160 / 8 -> 20 workgroups
 constexpr int kRsF32Block = 64;
 constexpr unsigned kRsF32ResidencyLds = 10 * 1024;   // 160 / 10 -> 16 workgroups
 
-// Vectors per lane per loop iteration (measured: 1 is best with full grids;
-// for the reduce, 2 and 4 were 1-3% slower on the layer shard and a 64M bucket).
-constexpr int kRsU = 1;
-constexpr int kFusedU = 1;
-constexpr int kAdamU = 1;
-constexpr int kGatherU = 1;
-
 // Owner k's parameters for a 1-D launch: contribution pointers moved to the
 // owner's slice (elem_units = shard length in units of p.g's element type).
 RsParams owner_slice(const RsParams& p, int k, int64_t elem_units) {
@@ -556,8 +574,8 @@ hipError_t rs_vec_launch(const RsParams& p, int n_shards, hipStream_t s) {
   for (int k = 0; k < n_shards; ++k) {
     const RsParams q = owner_slice(p, k, p.shard);
     constexpr int bs = ACC ? kRsAccBlock : kRsBlock;
-    dim3 grid(grid_x(p.shard >> 2, kRsU, 1, bs), 1);
-    hipLaunchKernelGGL((rs_vec_kernel<N, ACC, kRsU, bs>), grid, dim3(bs), ACC ? kRsAccResidencyLds : 0u, s, q);
+    dim3 grid(grid_x(p.shard >> 2, 1, bs), 1);
+    hipLaunchKernelGGL((rs_vec_kernel<N, ACC, bs>), grid, dim3(bs), ACC ? kRsAccResidencyLds : 0u, s, q);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -567,7 +585,7 @@ hipError_t rs_vec_launch(const RsParams& p, int n_shards, hipStream_t s) {
 template <bool ACC>
 hipError_t rs_dispatch(const RsParams& p, int n_shards, bool vec, hipStream_t s) {
   if (!vec) {
-    dim3 grid(grid_x(p.shard, 1, n_shards), n_shards);
+    dim3 grid(grid_x(p.shard, n_shards), n_shards);
     hipLaunchKernelGGL((rs_scalar_kernel<ACC>), grid, dim3(kBlock), 0, s, p);
     return hipGetLastError();
   }
@@ -592,7 +610,7 @@ template <int N, bool ACC>
 hipError_t rs_f32_vec_launch(const RsParams& p, int n_shards, hipStream_t s) {
   for (int k = 0; k < n_shards; ++k) {
     const RsParams q = owner_slice(p, k, 2 * p.shard);   // FP32 elements = 2 BF16 units
-    dim3 grid(grid_x(p.shard >> 2, 1, 1, kRsF32Block), 1);
+    dim3 grid(grid_x(p.shard >> 2, 1, kRsF32Block), 1);
     hipLaunchKernelGGL((rs_f32_vec_kernel<N, ACC, kRsF32Block>), grid, dim3(kRsF32Block), kRsF32ResidencyLds, s, q);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -603,7 +621,7 @@ hipError_t rs_f32_vec_launch(const RsParams& p, int n_shards, hipStream_t s) {
 template <bool ACC>
 hipError_t rs_f32_dispatch(const RsParams& p, int n_shards, bool vec, hipStream_t s) {
   if (!vec) {
-    dim3 grid(grid_x(p.shard, 1, n_shards), n_shards);
+    dim3 grid(grid_x(p.shard, n_shards), n_shards);
     hipLaunchKernelGGL((rs_f32_scalar_kernel<ACC>), grid, dim3(kBlock), 0, s, p);
     return hipGetLastError();
   }
@@ -621,8 +639,8 @@ hipError_t launch_reduce_scatter_f32(const RsParams& p, int n_shards, bool accum
 
 template <int N, int WD, bool WG, bool ACC>
 hipError_t fused_vec_launch(const FusedParams& p, int n_shards, hipStream_t s) {
-  dim3 grid(grid_x(p.shard >> 2, kFusedU, n_shards, kFusedBlock), n_shards);
-  hipLaunchKernelGGL((fused_vec_kernel<N, WD, WG, ACC, kFusedU, kFusedBlock>), grid, dim3(kFusedBlock),
+  dim3 grid(grid_x(p.shard >> 2, n_shards, kFusedBlock), n_shards);
+  hipLaunchKernelGGL((fused_vec_kernel<N, WD, WG, ACC, kFusedBlock>), grid, dim3(kFusedBlock),
                      kFusedResidencyLds, s, p);
   return hipGetLastError();
 }
@@ -655,7 +673,7 @@ int decay_mode(const zero_adam_scalars& s, const zero_adam_scalars* sdev) {
 hipError_t launch_fused(const FusedParams& p, int n_shards, bool write_grad, bool vec, hipStream_t s) {
   const int wd = decay_mode(p.s, p.sdev);
   if (!vec) {
-    dim3 grid(grid_x(p.shard, 1, n_shards), n_shards);
+    dim3 grid(grid_x(p.shard, n_shards), n_shards);
     if (wd == 2)
       hipLaunchKernelGGL((fused_scalar_kernel<2>), grid, dim3(kBlock), 0, s, p);
     else if (wd == 1)
@@ -692,11 +710,11 @@ hipError_t launch_fused(const FusedParams& p, int n_shards, bool write_grad, boo
 template <int WD, bool SC>
 hipError_t adam_launch(const AdamParams& a, bool vec, hipStream_t s) {
   if (vec) {
-    dim3 grid(grid_x(a.n >> 2, kAdamU, 1, kAdamBlock));
-    hipLaunchKernelGGL((adam_vec_kernel<WD, SC, kAdamU, kAdamBlock>), grid, dim3(kAdamBlock),
+    dim3 grid(grid_x(a.n >> 2, 1, kAdamBlock));
+    hipLaunchKernelGGL((adam_vec_kernel<WD, SC, kAdamBlock>), grid, dim3(kAdamBlock),
                        kAdamResidencyLds, s, a);
   } else {
-    dim3 grid(grid_x(a.n, 1, 1));
+    dim3 grid(grid_x(a.n, 1));
     hipLaunchKernelGGL((adam_scalar_kernel<WD, SC>), grid, dim3(kBlock), 0, s, a);
   }
   return hipGetLastError();
@@ -734,21 +752,21 @@ hipError_t launch_norm(NormParams& p, bool vec, hipStream_t s) {
 hipError_t launch_gather(const GatherParams& p, int n_shards, int path, hipStream_t s) {
   constexpr int bs = kGatherBlock;
   if (path == GATHER_V16) {
-    dim3 grid(grid_x(p.shard_bytes / 16, kGatherU, n_shards, bs), n_shards);
-    hipLaunchKernelGGL((gather_kernel<u32x4, kGatherU, bs>), grid, dim3(bs), 0, s, p);
+    dim3 grid(grid_x(p.shard_bytes / 16, n_shards, bs), n_shards);
+    hipLaunchKernelGGL((gather_kernel<u32x4, bs>), grid, dim3(bs), 0, s, p);
   } else if (path == GATHER_U32) {
-    dim3 grid(grid_x(p.shard_bytes / 4, kGatherU, n_shards, bs), n_shards);
-    hipLaunchKernelGGL((gather_kernel<uint32_t, kGatherU, bs>), grid, dim3(bs), 0, s, p);
+    dim3 grid(grid_x(p.shard_bytes / 4, n_shards, bs), n_shards);
+    hipLaunchKernelGGL((gather_kernel<uint32_t, bs>), grid, dim3(bs), 0, s, p);
   } else {
-    dim3 grid(grid_x(p.shard_bytes, kGatherU, n_shards, bs), n_shards);
-    hipLaunchKernelGGL((gather_kernel<uint8_t, kGatherU, bs>), grid, dim3(bs), 0, s, p);
+    dim3 grid(grid_x(p.shard_bytes, n_shards, bs), n_shards);
+    hipLaunchKernelGGL((gather_kernel<uint8_t, bs>), grid, dim3(bs), 0, s, p);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_x(n, 1, 1)), dim3(kBlock), 0, s, p, value, n);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_x(n, 1)), dim3(kBlock), 0, s, p, value, n);
   return hipGetLastError();
 }
 
