@@ -331,14 +331,14 @@ def run_flat(args, wl, numels, grad_scales=None, counts=None):
         "hbm_gbs_algorithmic": (2 * n + 30 + B_AG) * pad / (fg_ms * 1e-3) / 1e9,
     }
     # the separate-kernel step captured once into a HIP graph and replayed
-    # (the step's scalars copied to the device before each replay)
+    # (the graph's first kernel takes the step's scalars from a pinned ring)
     from zero_sharded_optimizer_reduce_amd.drivers import GraphedStep
     gs = GraphedStep(st, grads, w)
     gr_ms, _ = timed(lambda hp, sample: gs.step(hp), None)
     out["graph_variant"] = {
         "ms_per_step": gr_ms, "value": st.psi / (gr_ms * 1e-3),
-        "step": "reduce-scatter + 4 owner updates (scalars read from device memory) + all-gather, "
-                "captured once and replayed; a 36-byte scalar copy precedes each replay",
+        "step": "scalar fetch from a pinned ring + reduce-scatter + 4 owner updates (scalars read from "
+                "device memory) + all-gather, captured once and replayed",
         "hbm_gbs_algorithmic": step_bytes / (gr_ms * 1e-3) / 1e9}
     del gs
     out["next_rows"] = _next_rows(args, st, grads, w, wl, timed, T)

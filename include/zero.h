@@ -241,6 +241,32 @@ int zero_reduce_scatter_adam_dev(const uint16_t* const* rank_grads, const float*
                                  float* const* grad_out, const zero_adam_scalars* scalars_dev,
                                  void* stream);
 
+/* Scalar staging for captured steps, as a kernel instead of a copy: one
+ * single-lane kernel on `stream` copies slot (*cursor_dev mod ring_len) of a
+ * ring of zero_adam_scalars in pinned host memory into scalars_dev, then adds
+ * one to *cursor_dev.  A step captured into a HIP graph starts with this call
+ * (then the _dev calls read scalars_dev), so each replay takes the next slot
+ * with no host-to-device copy between replays.  Protocol: *cursor_dev is 0
+ * before the first replay (cleared by the caller before capture); the host
+ * writes step t's scalars (zero_adam_scalars_compute) into slot t mod
+ * ring_len before launching replay t, and rewrites a slot only after the
+ * replay that read it has completed.  The ring is read with system-scope
+ * loads when the kernel runs, so host writes made before the launch are seen.
+ *
+ *   ring_host    ring_len consecutive zero_adam_scalars in memory from
+ *                hipHostMalloc (pinned, mapped for the device), 4-byte aligned
+ *   ring_len     a power of two, 1..65536 (so that the slot sequence stays
+ *                the same when the 32-bit cursor wraps)
+ *   cursor_dev   device uint32_t, 4-byte aligned, read and written
+ *   scalars_dev  device zero_adam_scalars, 4-byte aligned, written
+ * Ownership: all four buffers belong to the caller.
+ * Errors: ZERO_ERR_ARG for NULL pointers, ring_len out of range, cursor and
+ * scalars overlapping, or a ring that is not one pinned host allocation
+ * holding ring_len structs (checked with the runtime's pointer attributes);
+ * ZERO_ERR_ALIGN for misaligned pointers.  Nothing is launched on error. */
+int zero_adam_scalars_fetch(const zero_adam_scalars* ring_host, int ring_len, uint32_t* cursor_dev,
+                            zero_adam_scalars* scalars_dev, void* stream);
+
 /* All-gather into a temporary full view ([slide] note 原 N47 and beat b2;
  * [essay] ZeRO-3 的一次完整计算; [blog] 三级分片, ZeRO-3): the owners'
  * shards, concatenated in owner order, form the full per-layer view.

@@ -71,6 +71,27 @@ int main() {
   EXPECT(check_adam_dev(p, m, v, b, gr, 4096, (const zero_adam_scalars*)(p + 4096 - 4), e) == ZERO_ERR_ARG);
   EXPECT(check_adam_dev(p, m, v, b, gr, 4096, (const zero_adam_scalars*)(gr + 8), e) == ZERO_OK);
   EXPECT(check_adam_dev(p, p + 16, v, b, gr, 4096, sd, e) == ZERO_ERR_ARG);   // buffers still checked
+  // the scalar ring of captured steps (memory types are checked by the entry point itself)
+  {
+    const zero_adam_scalars* ring = (const zero_adam_scalars*)P(0x900000);
+    uint32_t* cur = (uint32_t*)P(0xa00000);
+    zero_adam_scalars* out = (zero_adam_scalars*)P(0xb00000);
+    EXPECT(check_scalars_fetch(ring, 1, cur, out, e) == ZERO_OK);
+    EXPECT(check_scalars_fetch(ring, 8, cur, out, e) == ZERO_OK);
+    EXPECT(check_scalars_fetch((const zero_adam_scalars*)P(0x10000000), 1 << 16, cur, out, e) == ZERO_OK);
+    EXPECT(check_scalars_fetch(ring, 1 << 16, cur, out, e) == ZERO_ERR_ARG);   // 2.4 MB reach cursor and scalars
+    EXPECT(check_scalars_fetch(ring, 0, cur, out, e) == ZERO_ERR_ARG);
+    EXPECT(check_scalars_fetch(ring, 6, cur, out, e) == ZERO_ERR_ARG);
+    EXPECT(check_scalars_fetch(ring, 1 << 17, cur, out, e) == ZERO_ERR_ARG);
+    EXPECT(check_scalars_fetch(ring, -4, cur, out, e) == ZERO_ERR_ARG);
+    EXPECT(check_scalars_fetch(nullptr, 8, cur, out, e) == ZERO_ERR_ARG);
+    EXPECT(check_scalars_fetch(ring, 8, nullptr, out, e) == ZERO_ERR_ARG);
+    EXPECT(check_scalars_fetch(ring, 8, cur, nullptr, e) == ZERO_ERR_ARG);
+    EXPECT(check_scalars_fetch(ring, 8, (uint32_t*)P(0xa00002), out, e) == ZERO_ERR_ALIGN);
+    EXPECT(check_scalars_fetch(ring, 8, (uint32_t*)P(0xb00020), out, e) == ZERO_ERR_ARG);   // cursor in scalars
+    EXPECT(check_scalars_fetch(ring, 8, (uint32_t*)P(0xb00024), out, e) == ZERO_OK);        // just past them
+    EXPECT(check_scalars_fetch(ring, 8, (uint32_t*)P(0x900000 + 7 * 36), out, e) == ZERO_ERR_ARG);  // in the ring
+  }
   {
     const uint16_t* gg[2] = {(const uint16_t*)P(0x10000), (const uint16_t*)P(0x20000)};
     float wts[2] = {0.5f, 0.5f};

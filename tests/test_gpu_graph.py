@@ -8,7 +8,12 @@ memory when the kernels run):
 * a ShardedStep captured into a HIP graph and replayed over several steps
   (new contributions and new step counts each time, eager work and
   synchronisations between replays) equals the eager step after every replay;
-* invalid device-scalar arguments are rejected before anything is launched.
+* the same with the host queueing every step before the device runs the
+  first (ring slots reused under the completion events only);
+* zero_adam_scalars_fetch walks its ring slot by slot and sees slots the
+  host rewrote between calls;
+* invalid device-scalar and ring arguments are rejected before anything is
+  launched.
 """
 import numpy as np
 import pytest
@@ -112,7 +117,7 @@ def test_graph_replays_equal_eager_steps(fused):
     grads = [torch.empty(eager.psi_pad, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
     tmp = torch.empty(eager.psi_pad, device="cuda")
     g = GraphedStep(graphed, grads, w, fused=fused)
-    for t in range(1, 6):
+    for t in range(1, 2 * GraphedStep.RING + 4):   # every ring slot reused at least twice
         for r in range(n):
             gen.bf16_normal_(grads[r], 1e-3, t, r, tmp=tmp)
         hp = _hp(0.1 if t % 2 else 0.0, t)
@@ -126,6 +131,84 @@ def test_graph_replays_equal_eager_steps(fused):
         # unrelated eager work and a synchronisation before the next replay
         tmp.mul_(0.5).add_(1.0)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_replays_without_host_waits(fused):
+    # the host queues every step before the device has run the first one, so
+    # ring slots are rewritten only as the completion events allow
+    numels = [4096 * 5 + 8, 999]
+    n = 4
+    gen = S.DeviceGen(78)
+    eager, graphed = ShardedStep(numels, n), ShardedStep(numels, n)
+    master0 = gen.normal_(torch.empty(eager.psi_pad, device="cuda"), 0.02, 0)
+    eager.load_master(master0)
+    graphed.load_master(master0)
+    w = z.zero_rank_weights([4096, 3072, 4096, 2048], n)
+    grads = [gen.bf16_normal_(torch.empty(eager.psi_pad, dtype=torch.bfloat16, device="cuda"), 1e-3, 1, r)
+             for r in range(n)]
+    g = GraphedStep(graphed, grads, w, fused=fused)
+    steps = 3 * GraphedStep.RING + 1
+    hps = [_hp(0.1 if t % 3 else 0.0, t) for t in range(1, steps + 1)]
+    for hp in hps:
+        eager.step(grads, w, hp)
+    for hp in hps:
+        g.step(hp)
+    torch.cuda.synchronize()
+    for name in ("master", "exp_avg", "exp_avg_sq", "bf16", "grad"):
+        for k in range(n):
+            _same(getattr(eager, name)[k], getattr(graphed, name)[k], f"{name}[{k}] after {steps} steps")
+    _same(eager.view, graphed.view, "view")
+
+
+def test_scalars_fetch_walks_the_ring():
+    R = 4
+    F = z.ADAM_SCALARS_FLOATS
+    ring = torch.zeros(R, F, dtype=torch.float32, pin_memory=True)
+    for i in range(R):
+        z.adam_scalars_tensor(_hp(0.1 * (i % 2), i + 1), out=ring[i])
+    cursor = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dev = torch.zeros(F, device="cuda")
+    for c in range(3 * R + 1):
+        z.zero_adam_scalars_fetch(ring, cursor, dev)
+        torch.cuda.synchronize()
+        assert cursor.item() == c + 1
+        _same(dev.cpu(), ring[c % R], f"call {c}")
+        # rewrite the slot just read: the next pass over the ring must see the new values
+        z.adam_scalars_tensor(_hp(0.1, 100 + c), out=ring[c % R])
+
+
+def test_scalars_fetch_validation():
+    lib = z.load()
+    F = z.ADAM_SCALARS_FLOATS
+    ring = torch.zeros(4, F, dtype=torch.float32, pin_memory=True)
+    cursor = torch.zeros(2, dtype=torch.int32, device="cuda")
+    dev = torch.zeros(F, device="cuda")
+    rp, cp, dp = ring.data_ptr(), cursor.data_ptr(), dev.data_ptr()
+    pageable = np.zeros(4 * F, np.float32)
+    on_device = torch.zeros(4 * F, device="cuda")
+    assert lib.zero_adam_scalars_fetch(rp, 3, cp, dp, None) == _lib.ZERO_ERR_ARG       # not a power of two
+    assert lib.zero_adam_scalars_fetch(rp, 0, cp, dp, None) == _lib.ZERO_ERR_ARG
+    assert lib.zero_adam_scalars_fetch(rp, 1 << 17, cp, dp, None) == _lib.ZERO_ERR_ARG
+    assert lib.zero_adam_scalars_fetch(None, 4, cp, dp, None) == _lib.ZERO_ERR_ARG
+    assert lib.zero_adam_scalars_fetch(rp, 4, None, dp, None) == _lib.ZERO_ERR_ARG
+    assert lib.zero_adam_scalars_fetch(rp + 2, 4, cp, dp, None) == _lib.ZERO_ERR_ALIGN
+    assert lib.zero_adam_scalars_fetch(rp, 4, dp, dp, None) == _lib.ZERO_ERR_ARG       # cursor inside scalars
+    assert lib.zero_adam_scalars_fetch(pageable.ctypes.data, 4, cp, dp, None) == _lib.ZERO_ERR_ARG
+    assert lib.zero_adam_scalars_fetch(on_device.data_ptr(), 4, cp, dp, None) == _lib.ZERO_ERR_ARG
+    assert lib.zero_adam_scalars_fetch(rp, 1 << 16, cp, dp, None) == _lib.ZERO_ERR_ARG  # past the allocation
+    with pytest.raises(ValueError):
+        z.zero_adam_scalars_fetch(torch.zeros(4, F), cursor[:1], dev)                  # not pinned
+    with pytest.raises(ValueError):
+        z.zero_adam_scalars_fetch(torch.zeros(5, dtype=torch.float32, pin_memory=True), cursor[:1], dev)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(cursor) == 0 and torch.count_nonzero(dev) == 0           # nothing launched
+    # a valid call after the rejected ones: no error was left behind
+    z.adam_scalars_tensor(_hp(0.1, 7), out=ring[0])
+    z.zero_adam_scalars_fetch(ring, cursor[:1], dev)
+    torch.cuda.synchronize()
+    assert cursor[0].item() == 1 and cursor[1].item() == 0
+    _same(dev.cpu(), ring[0], "slot 0")
 
 
 def test_device_scalar_arguments_are_validated():

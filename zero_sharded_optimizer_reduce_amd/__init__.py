@@ -11,6 +11,7 @@ from .api import (  # noqa: F401
     ZeroOffload,
     adam_scalars_tensor,
     zero_adam_scalars_compute,
+    zero_adam_scalars_fetch,
     zero_adam_shard_step,
     zero_adam_shard_step_dev,
     zero_adam_shard_step_scaled,

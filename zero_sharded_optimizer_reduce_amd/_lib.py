@@ -47,6 +47,7 @@ SIGNATURES = {
                                            C.POINTER(AdamHparams), P]),
     "zero_adam_shard_step_dev": (C.c_int, [P, P, P, P, P, P, I64, P, P]),
     "zero_reduce_scatter_adam_dev": (C.c_int, [PP, FP, C.c_int, I64, C.c_int, PP, PP, PP, PP, PP, PP, P, P]),
+    "zero_adam_scalars_fetch": (C.c_int, [P, C.c_int, P, P, P]),
     "zero_all_gather_layer": (C.c_int, [PP, C.c_int, I64, P, P]),
     "zero_offload_create": (C.c_int, [C.c_int, I64, I64, P, PP, PP, C.POINTER(C.c_void_p)]),
     "zero_offload_stream": (C.c_int, [P, C.c_int, I64, C.c_int, FP, P, P, P, P,

@@ -272,6 +272,26 @@ def zero_reduce_scatter_adam_dev(rank_grads, rank_weights, master, exp_avg, exp_
           "zero_reduce_scatter_adam_dev")
 
 
+def zero_adam_scalars_fetch(ring_host: torch.Tensor, cursor_dev: torch.Tensor, scalars_dev: torch.Tensor,
+                            stream=None) -> None:
+    """One kernel on the stream: scalars_dev <- slot (cursor mod ring length)
+    of ring_host, then cursor + 1.  ring_host: a pinned CPU float32 tensor of
+    ring_len * ADAM_SCALARS_FLOATS elements (ring_len a power of two), one
+    adam_scalars_tensor per slot; cursor_dev: a one-element int32 device tensor,
+    zero before the first replay; scalars_dev: as for the _dev calls."""
+    if ring_host.device.type != "cpu" or ring_host.dtype != torch.float32 or not ring_host.is_contiguous():
+        raise ValueError("zero_adam_scalars_fetch: ring_host must be a contiguous CPU float32 tensor")
+    if not ring_host.is_pinned():
+        raise ValueError("zero_adam_scalars_fetch: ring_host must be pinned (pin_memory=True)")
+    if ring_host.numel() == 0 or ring_host.numel() % ADAM_SCALARS_FLOATS:
+        raise ValueError(f"zero_adam_scalars_fetch: ring_host must hold a multiple of {ADAM_SCALARS_FLOATS} floats")
+    cur = _dev(cursor_dev, "cursor_dev", (torch.int32,))
+    if cursor_dev.numel() != 1:
+        raise ValueError("zero_adam_scalars_fetch: cursor_dev must have one element")
+    check(load().zero_adam_scalars_fetch(ring_host.data_ptr(), ring_host.numel() // ADAM_SCALARS_FLOATS, cur,
+                                         _scalars_dev(scalars_dev), _stream(stream)), "zero_adam_scalars_fetch")
+
+
 def zero_all_gather_layer(shards: Sequence[torch.Tensor], full_view: torch.Tensor, stream=None) -> None:
     """full_view = concatenation of the shards' bytes in owner order."""
     n = len(shards)

@@ -85,6 +85,11 @@ hipError_t launch_gather(const GatherParams& p, int n_shards, int path, hipStrea
 // folds them in index order and derives the clip coefficient.
 hipError_t launch_norm(NormParams& p, bool vec, hipStream_t stream);
 
+// zero_adam_scalars_fetch: ring is the device-visible address of the pinned
+// host ring, ring_len a power of two.
+hipError_t launch_scalars_fetch(const zero_adam_scalars* ring, int ring_len, uint32_t* cursor,
+                                zero_adam_scalars* out, hipStream_t stream);
+
 // Fill n 32-bit words with `value` (used to poison released staging buffers
 // in the offload engine's debug mode).
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, int64_t n, hipStream_t stream);

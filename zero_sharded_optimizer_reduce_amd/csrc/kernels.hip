@@ -480,6 +480,27 @@ __global__ __launch_bounds__(BS) void gather_kernel(GatherParams p) {
   }
 }
 
+// ------------------------------------------- scalars of a captured step
+// One lane copies slot (*cursor mod len) of the host ring into *out and
+// advances the cursor.  The host rewrites ring slots between replays, so the
+// ring is read with system-scope loads (never served from a GPU cache); the
+// cursor, written only here, with agent-scope ones.  len is a power of two.
+constexpr int kScalarWords = static_cast<int>(sizeof(zero_adam_scalars) / sizeof(uint32_t));
+static_assert(sizeof(zero_adam_scalars) == kScalarWords * sizeof(uint32_t), "scalars are 32-bit words");
+
+__global__ __launch_bounds__(64) void scalars_fetch_kernel(const uint32_t* ring, uint32_t len, uint32_t* cursor,
+                                                           uint32_t* out) {
+  if (threadIdx.x != 0) return;
+  const uint32_t c = __hip_atomic_load(cursor, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t* src = ring + static_cast<size_t>(c & (len - 1)) * kScalarWords;
+  uint32_t w[kScalarWords];
+#pragma unroll
+  for (int i = 0; i < kScalarWords; ++i) w[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+#pragma unroll
+  for (int i = 0; i < kScalarWords; ++i) out[i] = w[i];
+  __hip_atomic_store(cursor, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __global__ __launch_bounds__(kBlock) void fill_u32_kernel(uint32_t* p, uint32_t value, int64_t n) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * kBlock)
@@ -761,6 +782,13 @@ hipError_t launch_gather(const GatherParams& p, int n_shards, int path, hipStrea
     dim3 grid(grid_x(p.shard_bytes, n_shards, bs), n_shards);
     hipLaunchKernelGGL((gather_kernel<uint8_t, bs>), grid, dim3(bs), 0, s, p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_scalars_fetch(const zero_adam_scalars* ring, int ring_len, uint32_t* cursor,
+                                zero_adam_scalars* out, hipStream_t s) {
+  hipLaunchKernelGGL(scalars_fetch_kernel, dim3(1), dim3(64), 0, s, reinterpret_cast<const uint32_t*>(ring),
+                     static_cast<uint32_t>(ring_len), cursor, reinterpret_cast<uint32_t*>(out));
   return hipGetLastError();
 }
 

@@ -232,6 +232,22 @@ int check_adam(const float* master, const float* exp_avg, const float* exp_avg_s
   return check_adam_buffers(master, exp_avg, exp_avg_sq, bf16_out, grad, n, e);
 }
 
+int check_scalars_fetch(const zero_adam_scalars* ring_host, int ring_len, const uint32_t* cursor_dev,
+                        const zero_adam_scalars* scalars_dev, Err& e) {
+  if (!ring_host || !cursor_dev || !scalars_dev) return set_err(e, ZERO_ERR_ARG, "scalars_fetch: NULL pointer");
+  if (ring_len < 1 || ring_len > (1 << 16) || (ring_len & (ring_len - 1)) != 0)
+    return set_err(e, ZERO_ERR_ARG, "scalars_fetch: ring_len=%d is not a power of two in 1..65536", ring_len);
+  if ((reinterpret_cast<uintptr_t>(ring_host) | reinterpret_cast<uintptr_t>(cursor_dev) |
+       reinterpret_cast<uintptr_t>(scalars_dev)) & 3u)
+    return set_err(e, ZERO_ERR_ALIGN, "scalars_fetch: pointers must be 4-byte aligned");
+  const Range ring = range_of(ring_host, static_cast<int64_t>(ring_len) * sizeof(zero_adam_scalars));
+  const Range cur = range_of(cursor_dev, sizeof(uint32_t));
+  const Range out = range_of(scalars_dev, sizeof(zero_adam_scalars));
+  if (overlaps(cur, out) || overlaps(ring, out) || overlaps(ring, cur))
+    return set_err(e, ZERO_ERR_ARG, "scalars_fetch: ring, cursor and scalars must not overlap");
+  return ZERO_OK;
+}
+
 int check_adam_dev(const float* master, const float* exp_avg, const float* exp_avg_sq,
                    const uint16_t* bf16_out, const float* grad, int64_t n,
                    const zero_adam_scalars* scalars_dev, Err& e) {

@@ -52,6 +52,11 @@ int check_reduce_scatter_adam_dev(const uint16_t* const* rank_grads, const float
                                   float* const* exp_avg, float* const* exp_avg_sq,
                                   uint16_t* const* bf16_out, const float* const* grad_acc,
                                   float* const* grad_out, const zero_adam_scalars* scalars_dev, Err& e);
+// zero_adam_scalars_fetch without the memory-type check (which needs the
+// runtime): non-NULL, 4-byte aligned, ring_len a power of two in 1..65536,
+// no overlap between ring, cursor and scalars.
+int check_scalars_fetch(const zero_adam_scalars* ring_host, int ring_len, const uint32_t* cursor_dev,
+                        const zero_adam_scalars* scalars_dev, Err& e);
 // The device scale of zero_adam_shard_step_scaled: non-NULL, 4-byte aligned,
 // outside every buffer the update writes.
 int check_adam_scale(const float* grad_scale, const float* master, const float* exp_avg,

@@ -312,6 +312,52 @@ int zero_reduce_scatter_adam_dev(const uint16_t* const* rank_grads, const float*
                       bf16_out, grad_acc, grad_out, unused, scalars_dev, stream, "zero_reduce_scatter_adam_dev");
 }
 
+// The ring must be pinned host memory mapped for the device, with all
+// ring_len structs inside that one allocation: the kernel reads it through
+// the device mapping, and a pageable or short ring would fault there.  On
+// success *dev_ring is the ring's device-visible address.
+static int pinned_ring(const zero_adam_scalars* ring, int ring_len, const zero_adam_scalars** dev_ring) {
+  hipPointerAttribute_t at;
+  memset(&at, 0, sizeof at);
+  if (hipPointerGetAttributes(&at, ring) != hipSuccess || at.type != hipMemoryTypeHost || !at.devicePointer ||
+      !at.hostPointer) {
+    (void)hipGetLastError();  // leave no error behind for the next launch check to report
+    return fail(ZERO_ERR_ARG, "zero_adam_scalars_fetch: ring_host is not pinned host memory (hipHostMalloc)");
+  }
+  void* start = nullptr;
+  size_t size = 0;
+  if (hipPointerGetAttribute(&start, HIP_POINTER_ATTRIBUTE_RANGE_START_ADDR,
+                             reinterpret_cast<hipDeviceptr_t>(const_cast<zero_adam_scalars*>(ring))) != hipSuccess ||
+      hipPointerGetAttribute(&size, HIP_POINTER_ATTRIBUTE_RANGE_SIZE,
+                             reinterpret_cast<hipDeviceptr_t>(const_cast<zero_adam_scalars*>(ring))) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(ZERO_ERR_ARG, "zero_adam_scalars_fetch: the ring's pinned allocation could not be determined");
+  }
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(start), hi = lo + size;
+  const uintptr_t r0 = reinterpret_cast<uintptr_t>(ring);
+  const uintptr_t r1 = r0 + static_cast<uintptr_t>(ring_len) * sizeof(zero_adam_scalars);
+  if (r0 < lo || r1 > hi || r1 < r0)
+    return fail(ZERO_ERR_ARG, "zero_adam_scalars_fetch: ring_len structs do not fit in the ring's pinned allocation");
+  // the device address of `ring`, whether the runtime reports the pointers of
+  // the allocation's start or of the queried address
+  const intptr_t off = static_cast<intptr_t>(r0 - reinterpret_cast<uintptr_t>(at.hostPointer));
+  *dev_ring = reinterpret_cast<const zero_adam_scalars*>(static_cast<char*>(at.devicePointer) + off);
+  return ZERO_OK;
+}
+
+int zero_adam_scalars_fetch(const zero_adam_scalars* ring_host, int ring_len, uint32_t* cursor_dev,
+                            zero_adam_scalars* scalars_dev, void* stream) {
+  TraceRange tr("zero_adam_scalars_fetch");
+  Err e;
+  int st = check_scalars_fetch(ring_host, ring_len, cursor_dev, scalars_dev, e);
+  if (st) return fail(st, e.msg);
+  const zero_adam_scalars* dev_ring = nullptr;
+  st = pinned_ring(ring_host, ring_len, &dev_ring);
+  if (st) return st;
+  return hip_status(launch_scalars_fetch(dev_ring, ring_len, cursor_dev, scalars_dev, static_cast<hipStream_t>(stream)),
+                    "zero_adam_scalars_fetch");
+}
+
 int zero_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* rank_weights,
                              int n_ranks, int64_t numel, int n_shards, float* const* master,
                              float* const* exp_avg, float* const* exp_avg_sq,

@@ -23,9 +23,9 @@ from typing import Optional, Sequence
 
 import torch
 
-from .api import (ADAM_SCALARS_FLOATS, ZeroOffload, adam_scalars_tensor, zero_adam_shard_step,
-                  zero_adam_shard_step_dev, zero_all_gather_layer, zero_reduce_scatter, zero_reduce_scatter_adam,
-                  zero_reduce_scatter_adam_dev, zero_shard_layout)
+from .api import (ADAM_SCALARS_FLOATS, ZeroOffload, adam_scalars_tensor, zero_adam_scalars_fetch,
+                  zero_adam_shard_step, zero_adam_shard_step_dev, zero_all_gather_layer, zero_reduce_scatter,
+                  zero_reduce_scatter_adam, zero_reduce_scatter_adam_dev, zero_shard_layout)
 
 
 def _empty(n, dtype, device):
@@ -76,28 +76,31 @@ class GraphedStep:
     """A ShardedStep captured once into a HIP graph (torch.cuda.CUDAGraph) and
     replayed at every step: reduce-scatter, the owners' updates, all-gather
     (or the fused reduce + update storing the reduced shards, then the
-    all-gather).  The updates read the step's scalars from a device struct, so
-    each step() computes them on the host, copies them in on the replay
-    stream and replays; results are bit-identical to ShardedStep.step with the
-    same hyper-parameters.  The caller writes each step's contributions into
-    the captured rank_grads buffers; the rank weights are those of the capture.
-    Host staging for the scalars is a ring of pinned buffers, each reused only
-    after the copy that last read it has run."""
+    all-gather).  The updates read the step's scalars from a device struct
+    that the graph's first kernel (zero_adam_scalars_fetch) fills from a ring
+    of pinned host slots, taking the next slot at every replay; step() writes
+    this step's scalars into that slot and replays, with no copy call between
+    replays.  Results are bit-identical to ShardedStep.step with the same
+    hyper-parameters.  The caller writes each step's contributions into the
+    captured rank_grads buffers; the rank weights are those of the capture.
+    A slot is rewritten only after the replay that read it has completed."""
 
-    RING = 4
+    RING = 8          # ring slots: a power of two, as the fetch kernel requires
+    EVENT_EVERY = 4   # replays per completion event (RING // 2)
 
     def __init__(self, st: ShardedStep, rank_grads, weights, fused: bool = False):
         self.st = st
         self.rank_grads = list(rank_grads)
         dev = st.device
         self.scalars = torch.zeros(ADAM_SCALARS_FLOATS, dtype=torch.float32, device=dev)
-        self._ring = [torch.empty(ADAM_SCALARS_FLOATS, dtype=torch.float32, pin_memory=True)
-                      for _ in range(self.RING)]
-        self._copied = [None] * self.RING
-        self._slot = 0
+        self.cursor = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.ring = torch.zeros(self.RING, ADAM_SCALARS_FLOATS, dtype=torch.float32, pin_memory=True)
+        self._events = {}   # group of EVENT_EVERY replays -> event recorded after its last replay
+        self._t = 0
         self.graph = torch.cuda.CUDAGraph()
         torch.cuda.synchronize(dev)
         with torch.cuda.graph(self.graph):
+            zero_adam_scalars_fetch(self.ring, self.cursor, self.scalars)
             if fused:
                 zero_reduce_scatter_adam_dev(self.rank_grads, weights, st.master, st.exp_avg, st.exp_avg_sq,
                                              st.bf16, self.scalars, grad_out=st.grad)
@@ -110,17 +113,23 @@ class GraphedStep:
         torch.cuda.synchronize(dev)
 
     def step(self, hp):
-        """One step on the current stream: this step's scalars, then the replay."""
-        i = self._slot
-        self._slot = (i + 1) % self.RING
-        if self._copied[i] is not None:
-            self._copied[i].synchronize()
-        adam_scalars_tensor(hp, out=self._ring[i])
-        self.scalars.copy_(self._ring[i], non_blocking=True)
-        ev = torch.cuda.Event()
-        ev.record()
-        self._copied[i] = ev
+        """One step on the current stream: this step's scalars into its ring
+        slot, then the replay.  Slot t mod RING was last read by replay
+        t - RING.  At the first step of each group of EVENT_EVERY steps the
+        host waits for the event recorded after replay t - RING +
+        EVENT_EVERY - 1, which frees the slots of this step and of the next
+        EVENT_EVERY - 1 steps; the host stays up to RING - EVENT_EVERY + 1
+        replays ahead of the device."""
+        t = self._t
+        if t >= self.RING and (t - self.RING) % self.EVENT_EVERY == 0:
+            self._events.pop((t - self.RING) // self.EVENT_EVERY).synchronize()
+        adam_scalars_tensor(hp, out=self.ring[t % self.RING])
         self.graph.replay()
+        if t % self.EVENT_EVERY == self.EVENT_EVERY - 1:
+            ev = torch.cuda.Event()
+            ev.record()
+            self._events[t // self.EVENT_EVERY] = ev
+        self._t = t + 1
         return self.st.view[: self.st.psi]
 
 
