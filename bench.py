@@ -23,6 +23,8 @@ oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import contextlib
+import gc
 import hashlib
 import json
 import os
@@ -78,6 +80,26 @@ def _roofline(kernel, workload, ms, params):
             "kernel": kernel, "algorithmic_bytes_per_launch": B_ADAM * params}
 
 
+@contextlib.contextmanager
+def no_gc():
+    """A timed region without Python's cyclic garbage collector: a full
+    collection over the objects that torch, numpy and the CPU baseline leave
+    (about 170k) pauses the launching thread for about 40 ms.  The host
+    queues a step in well under a millisecond but is only a few tens of
+    milliseconds ahead of the GPU early in a loop, so such a pause lets the
+    GPU run dry (measured: one 40 ms collection at step 19 of the 7B-layer
+    loop added 0.15 ms to the average step).  Garbage is collected before
+    the region instead."""
+    gc.collect()
+    enabled = gc.isenabled()
+    gc.disable()
+    try:
+        yield
+    finally:
+        if enabled:
+            gc.enable()
+
+
 def _mean(xs):
     return float(sum(xs) / max(1, len(xs)))
 
@@ -118,11 +140,12 @@ def copy_ceiling_gbs(nbytes=1 << 30, reps=20):
     for _ in range(3):
         z.zero_all_gather_layer([src], dst)
     T = Timer()
-    a = T.ev()
-    for _ in range(reps):
-        z.zero_all_gather_layer([src], dst)
-    b = T.ev()
-    torch.cuda.synchronize()
+    with no_gc():
+        a = T.ev()
+        for _ in range(reps):
+            z.zero_all_gather_layer([src], dst)
+        b = T.ev()
+        torch.cuda.synchronize()
     ms = a.elapsed_time(b) / reps
     del src, dst
     return 2 * nbytes / (ms * 1e-3) / 1e9
@@ -241,14 +264,16 @@ def run_flat(args, wl, numels, grad_scales=None, counts=None):
             t += 1
             step_fn(wl.hparams(step=t), None)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        start = T.ev()
-        for i in range(args.steps):
-            t += 1
-            step_fn(wl.hparams(step=t), phase_name if i % SAMPLE_EVERY == 0 else None)
-        stop = T.ev()
-        torch.cuda.synchronize()
-        return start.elapsed_time(stop) / args.steps, time.perf_counter() - t0
+        with no_gc():
+            t0 = time.perf_counter()
+            start = T.ev()
+            for i in range(args.steps):
+                t += 1
+                step_fn(wl.hparams(step=t), phase_name if i % SAMPLE_EVERY == 0 else None)
+            stop = T.ev()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        return start.elapsed_time(stop) / args.steps, wall
 
     def sep_step(hp, sample):
         st.reduce_scatter(grads, w)
@@ -268,17 +293,18 @@ def run_flat(args, wl, numels, grad_scales=None, counts=None):
     ms_step, wall = timed(sep_step, "update4")
     adam_ms = T.ms("update4") / n
     # breakdown pass for the reduce-scatter and the all-gather (not the timed region)
-    for _ in range(max(4, args.steps // SAMPLE_EVERY)):
-        t += 1
-        a = T.ev()
-        st.reduce_scatter(grads, w)
-        b = T.ev()
-        st.update(wl.hparams(step=t))
-        c = T.ev()
-        st.all_gather()
-        T.span("rs", a, b)
-        T.span("ag", c, T.ev())
-    torch.cuda.synchronize()
+    with no_gc():
+        for _ in range(max(4, args.steps // SAMPLE_EVERY)):
+            t += 1
+            a = T.ev()
+            st.reduce_scatter(grads, w)
+            b = T.ev()
+            st.update(wl.hparams(step=t))
+            c = T.ev()
+            st.all_gather()
+            T.span("rs", a, b)
+            T.span("ag", c, T.ev())
+        torch.cuda.synchronize()
     pad = st.psi_pad
     step_bytes = (B_RS(n) + B_ADAM + B_AG) * pad
     rs_ms, ag_ms = T.ms("rs"), T.ms("ag")
@@ -385,11 +411,12 @@ def _next_rows(args, st, grads, w, wl, timed, T):
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
-        a = T.ev()
-        for _ in range(reps):
-            fn()
-        b = T.ev()
-        torch.cuda.synchronize()
+        with no_gc():
+            a = T.ev()
+            for _ in range(reps):
+                fn()
+            b = T.ev()
+            torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
     reps = max(4, args.steps // 4)
@@ -468,14 +495,16 @@ def run_owner_share(args):
             t += 1
             step_fn(wl.hparams(step=t), False)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        start = T.ev()
-        for i in range(args.steps):
-            t += 1
-            step_fn(wl.hparams(step=t), i % SAMPLE_EVERY == 0)
-        stop = T.ev()
-        torch.cuda.synchronize()
-        return start.elapsed_time(stop) / args.steps, time.perf_counter() - t0
+        with no_gc():
+            t0 = time.perf_counter()
+            start = T.ev()
+            for i in range(args.steps):
+                t += 1
+                step_fn(wl.hparams(step=t), i % SAMPLE_EVERY == 0)
+            stop = T.ev()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        return start.elapsed_time(stop) / args.steps, wall
 
     assert st.bounds[0][1] - st.bounds[0][0] == B
     ms_step, wall = timed(sep_step)
@@ -552,16 +581,18 @@ def run_chain(args):
             t += 1
             step(t, fused=fused)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        marks = [T.ev()]
-        for _ in range(args.steps):
-            t += 1
-            step(t, marks, fused=fused)
-            marks.append(T.ev())
-        torch.cuda.synchronize()
+        with no_gc():
+            t0 = time.perf_counter()
+            marks = [T.ev()]
+            for _ in range(args.steps):
+                t += 1
+                step(t, marks, fused=fused)
+                marks.append(T.ev())
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
         fwd = sum(marks[2 * i].elapsed_time(marks[2 * i + 1]) for i in range(args.steps)) / args.steps
         tot = marks[0].elapsed_time(marks[-1]) / args.steps
-        return tot, fwd, time.perf_counter() - t0
+        return tot, fwd, wall
 
     ms_step, fwd_ms, wall = timed(False)
     bwd_ms = ms_step - fwd_ms
@@ -681,13 +712,14 @@ def run_offload(args):
             st.sync()
         torch.cuda.synchronize()
         times = []
-        for _ in range(args.steps):
-            t += 1
-            t0 = time.perf_counter()
-            st.step(produce, M, w, wl.hparams(step=t), fuse_last=fuse_last)
-            st.sync()
-            torch.cuda.synchronize()
-            times.append(time.perf_counter() - t0)
+        with no_gc():
+            for _ in range(args.steps):
+                t += 1
+                t0 = time.perf_counter()
+                st.step(produce, M, w, wl.hparams(step=t), fuse_last=fuse_last)
+                st.sync()
+                torch.cuda.synchronize()
+                times.append(time.perf_counter() - t0)
         return 1e3 * _mean(times)
 
     torch.cuda.synchronize()
