@@ -25,3 +25,28 @@ def test_cpu_baseline_fields():
     assert out["value"] > 0 and out["cores"] >= 1
     assert out["single_thread"]["cores"] == 1 and out["single_thread"]["value"] > 0
     assert "2^22" in out["sample"]
+
+
+def test_timed_regions_run_without_the_cyclic_collector():
+    # a full collection inside a timed loop stalls the launching thread long
+    # enough for the GPU to run dry; the region turns it off and restores it
+    import gc
+
+    import bench
+    assert gc.isenabled()
+    with bench.no_gc():
+        assert not gc.isenabled()
+    assert gc.isenabled()
+    try:
+        with bench.no_gc():
+            raise RuntimeError("inside")
+    except RuntimeError:
+        pass
+    assert gc.isenabled()
+    gc.disable()
+    try:
+        with bench.no_gc():
+            assert not gc.isenabled()
+        assert not gc.isenabled()      # a caller's own setting is kept
+    finally:
+        gc.enable()

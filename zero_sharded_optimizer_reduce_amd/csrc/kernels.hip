@@ -15,6 +15,7 @@
 // each kernel.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstdlib>
 
@@ -58,9 +59,10 @@ __device__ __forceinline__ void st_nt(T v, T* p) { __builtin_nontemporal_store(v
 // scalar registers and every lane offset is below 4 KiB), with the store bits
 // nt and sc1 (device scope); without it the plain non-temporal store is used.
 // Same-box A/B on MI355X: with sc1 the update, the fused kernel (without the
-// gradient output), the accumulate-mode reduce and the gather ran 1.4-3.6%
+// gradient output), the accumulate-mode reduce and the gather ran 1.0-3.6%
 // faster; the plain reduce, the FP32-contribution reduce and the fused kernel
-// storing the gradient ran 0.4-1.8% slower, so they keep the plain store.
+// storing the gradient ran 0.4-1.8% slower, so they keep the plain store
+// (system scope, sc0|sc1, measured the same as sc1).
 // The buffer forms are compiler intrinsics (not inline assembly), so the
 // compiler schedules them and resolves their register hazards.
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -527,17 +529,19 @@ int blocks_per_cu() {
   return v;
 }
 
+// Compute units of the current device, cached per device (calls from several
+// threads may fill a slot concurrently; they store the same value).
 int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int cus = 0;
+  int cus = cache[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
-    cache[dev] = cus;
+    cache[dev].store(cus, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return cus;
 }
 
 // Blocks along x for `units` work items per owner, each block covering bs of
