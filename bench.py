@@ -75,8 +75,11 @@ def _traffic(kernel: str, workload: str, launch_params: int):
 
 def _roofline(kernel, workload, ms, params):
     achieved = B_ADAM * params / (ms * 1e-3) / 1e9
+    traffic = _traffic(kernel, workload, params)
     return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS, "traffic": _traffic(kernel, workload, params),
+            "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+            # the counters' bytes over the same measured launch time
+            "traffic_gbs": None if traffic is None else traffic / (ms * 1e-3) / 1e9,
             "kernel": kernel, "algorithmic_bytes_per_launch": B_ADAM * params}
 
 
