@@ -48,6 +48,7 @@ extern "C" {
 
 #define ZERO_MAX_RANKS 16   /* upper bound on n_ranks and n_shards */
 #define ZERO_NORM_BLOCKS 1024  /* partial sums per shard in zero_grad_norm_sq */
+#define ZERO_OFFLOAD_MAX_CHUNKS 65536  /* upper bound on ceil(shard/chunk) of an offload handle */
 
 typedef enum zero_status {
   ZERO_OK = 0,
@@ -315,8 +316,10 @@ int zero_all_gather_layer(const void* const* shards, int n_shards, int64_t shard
  *   micro-batches 0..mb-1 only.
  * zero_offload_sync: waits for every queued copy and kernel of the handle; the
  *   host shard may be read after it returns.
- * Errors: ZERO_ERR_ARG / ZERO_ERR_ALIGN / ZERO_ERR_SIZE for bad arguments,
- * ZERO_ERR_STATE for a chunk out of range, a REDUCE with mb > 0 for a chunk
+ * Errors: ZERO_ERR_ARG / ZERO_ERR_ALIGN / ZERO_ERR_SIZE for bad arguments
+ * (ZERO_ERR_SIZE also for more than ZERO_OFFLOAD_MAX_CHUNKS chunks: the handle
+ * keeps two events per chunk, or when the handle's host memory cannot be
+ * allocated), ZERO_ERR_STATE for a chunk out of range, a REDUCE with mb > 0 for a chunk
  * that has no earlier micro-batch, or an ADAM for a chunk never reduced;
  * ZERO_ERR_HIP on runtime failures. */
 typedef struct zero_offload zero_offload;

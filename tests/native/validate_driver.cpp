@@ -157,6 +157,14 @@ int main() {
   EXPECT(check_offload_create(4, 1 << 20, 1 << 18, (const float*)P(0x5000), slots, stage, e) == ZERO_OK);
   uint16_t* slots_over[2] = {(uint16_t*)P(0x100000), (uint16_t*)P(0x800000)};
   EXPECT(check_offload_create(4, 1 << 20, 1 << 20, (const float*)P(0x5000), slots_over, stage, e) == ZERO_ERR_ARG);
+  // at most ZERO_OFFLOAD_MAX_CHUNKS chunks (the handle holds two events per chunk)
+  uint16_t* small_slots[2] = {(uint16_t*)P(0x100000), (uint16_t*)P(0x200000)};
+  float* small_stage[2] = {(float*)P(0x300000), (float*)P(0x400000)};
+  EXPECT(check_offload_create(4, 65536LL * 16, 16, (const float*)P(0x5000), small_slots, small_stage, e) == ZERO_OK);
+  EXPECT(check_offload_create(4, 65536LL * 16 + 1, 16, (const float*)P(0x5000), small_slots, small_stage, e) ==
+         ZERO_ERR_SIZE);
+  EXPECT(check_offload_create(4, 2000000000LL, 1, (const float*)P(0x5000), small_slots, small_stage, e) ==
+         ZERO_ERR_SIZE);
   if (fails) return 1;
   std::printf("ok\n");
   return 0;

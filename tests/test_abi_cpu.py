@@ -29,6 +29,18 @@ def test_every_declared_symbol_is_exported(libzero):
     assert set(_lib.SIGNATURES) == set(names)
 
 
+def test_binding_constants_match_the_header():
+    from zero_sharded_optimizer_reduce_amd import _lib
+    src = open(HEADER).read()
+    defines = dict(re.findall(r"^#define\s+(ZERO_\w+)\s+(\d+)", src, flags=re.M))
+    assert {"ZERO_MAX_RANKS", "ZERO_NORM_BLOCKS", "ZERO_OFFLOAD_MAX_CHUNKS"} <= set(defines)
+    for name, value in defines.items():
+        assert getattr(_lib, name) == int(value), name
+    enums = dict(re.findall(r"\b(ZERO_(?:OK|ERR_\w+|OFFLOAD_\w+))\s*=\s*(-?\d+)", src))
+    for name, value in enums.items():
+        assert getattr(_lib, name) == int(value), name
+
+
 def test_status_strings(libzero):
     for st in (0, -1, -2, -3, -4, -5):
         assert libzero.zero_status_string(st).startswith(b"ZERO_")

@@ -16,6 +16,7 @@ from gpu_helpers import assert_grad_exact, assert_state_close, bf16_to_dev, bf16
 pytestmark = pytest.mark.gpu
 
 z = pytest.importorskip("zero_sharded_optimizer_reduce_amd")
+from zero_sharded_optimizer_reduce_amd import _lib  # noqa: E402
 from zero_sharded_optimizer_reduce_amd.drivers import OffloadStep  # noqa: E402
 
 
@@ -101,3 +102,10 @@ def test_offload_misuse_is_rejected():
     st.engine.reduce(0, 0, w)
     st.sync()
     st.engine.close()
+    # more chunks than a handle may hold (two events per chunk)
+    chunk = 16
+    host = torch.zeros(_lib.ZERO_OFFLOAD_MAX_CHUNKS * chunk + 1, dtype=torch.float32, pin_memory=True)
+    slots = [torch.zeros(4 * chunk, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    stage = [torch.zeros(chunk, device="cuda") for _ in range(2)]
+    with pytest.raises(z.ZeroError, match="ZERO_ERR_SIZE"):
+        z.zero_offload_create(4, host.numel(), chunk, host, slots, stage)

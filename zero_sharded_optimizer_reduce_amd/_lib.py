@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzero.so"
 ZERO_OK, ZERO_ERR_ARG, ZERO_ERR_ALIGN, ZERO_ERR_SIZE, ZERO_ERR_HIP, ZERO_ERR_STATE = 0, -1, -2, -3, -4, -5
 ZERO_MAX_RANKS = 16
 ZERO_NORM_BLOCKS = 1024
+ZERO_OFFLOAD_MAX_CHUNKS = 65536
 ZERO_OFFLOAD_REDUCE, ZERO_OFFLOAD_ADAM, ZERO_OFFLOAD_REDUCE_ADAM = 0, 1, 2
 
 

@@ -22,6 +22,7 @@
 #include <chrono>
 #include <cstdlib>
 #include <cstring>
+#include <new>
 #include <thread>
 #include <vector>
 
@@ -131,7 +132,8 @@ int zero_offload_create(int n_ranks, int64_t shard_numel, int64_t chunk_numel,
   int st = check_offload_create(n_ranks, shard_numel, chunk_numel, host_shard_pinned, slot_contrib,
                                 slot_f32, e);
   if (st) return fail(st, e.msg);
-  zero_offload* h = new zero_offload();
+  zero_offload* h = new (std::nothrow) zero_offload();
+  if (!h) return fail(ZERO_ERR_SIZE, "offload_create: out of host memory");
   h->n_ranks = n_ranks;
   h->shard = shard_numel;
   h->chunk = chunk_numel;
@@ -146,13 +148,18 @@ int zero_offload_create(int n_ranks, int64_t shard_numel, int64_t chunk_numel,
   h->delay_arg = h->dbg.delay_us;
   const char* p = getenv("ZERO_OFFLOAD_DEBUG_POISON");
   h->dbg.poison = p && atoi(p) != 0;
-  h->host_written.resize(h->n_chunks);
-  h->host_read.resize(h->n_chunks);
-  h->last_mb.assign(h->n_chunks, -1);
   auto cleanup = [&](int status) {
     zero_offload_destroy(h);
     return status;
   };
+  try {
+    h->host_written.resize(h->n_chunks);
+    h->host_read.resize(h->n_chunks);
+    h->last_mb.assign(h->n_chunks, -1);
+  } catch (const std::bad_alloc&) {   // nothing may propagate through the C ABI
+    zero_offload_destroy(h);
+    return fail(ZERO_ERR_SIZE, "offload_create: out of host memory");
+  }
   hipError_t err = hipGetDevice(&h->device);
   if (err == hipSuccess) err = hipStreamCreateWithFlags(&h->h2d, hipStreamNonBlocking);
   if (err == hipSuccess) err = hipStreamCreateWithFlags(&h->d2h, hipStreamNonBlocking);

@@ -331,6 +331,8 @@ int check_offload_create(int n_ranks, int64_t shard_numel, int64_t chunk_numel,
     return set_err(e, ZERO_ERR_ARG, "offload_create: sizes must be positive");
   if (mul_overflows(chunk_numel, 2 * (int64_t)n_ranks) || mul_overflows(shard_numel, 4))
     return set_err(e, ZERO_ERR_SIZE, "offload_create: size overflow");
+  if ((shard_numel - 1) / chunk_numel + 1 > ZERO_OFFLOAD_MAX_CHUNKS)
+    return set_err(e, ZERO_ERR_SIZE, "offload_create: more than %d chunks", ZERO_OFFLOAD_MAX_CHUNKS);
   for (int s = 0; s < 2; ++s) {
     if (reinterpret_cast<uintptr_t>(slot_contrib[s]) & 1u || reinterpret_cast<uintptr_t>(slot_f32[s]) & 3u)
       return set_err(e, ZERO_ERR_ALIGN, "offload_create: slot %d misaligned", s);
