@@ -566,15 +566,19 @@ constexpr int kGatherBlock = 64;
 
 // Residency caps.  The update and the fused kernel use no LDS, but their
 // launches reserve this many bytes of it per workgroup, so that at most
-// 160 KiB / bytes workgroups (one wave each) are resident per CU: 12 for the
-// update (8 streams), 10 for the fused kernel (11 streams).  With fewer
+// 160 KiB / bytes workgroups (one wave each) are resident per CU: 10 for the
+// update (8 streams) and for the fused kernel (11 streams), 8 for the fused
+// kernel that also stores the reduced gradient (12 streams).  With fewer
 // requests in flight the HBM keeps more row hits: measured on MI355X, the
-// update goes from 6.1-6.2 to 6.5-6.6 TB/s, the fused kernel from 5.8-6.0 to
-// 6.55 TB/s.  The plain reduce (5 streams) and the gather (2) are fastest
-// without a cap.  The byte counts are multiples of 1 KiB and give the same count under
-// any allocation granularity up to 1 KiB.
-constexpr unsigned kAdamResidencyLds = 13 * 1024;    // 160 / 13 -> 12 workgroups
-constexpr unsigned kFusedResidencyLds = 16 * 1024;   // 160 / 16 -> 10 workgroups
+// update goes from 6.1-6.2 TB/s uncapped to 6.72-6.75 TB/s, the fused kernel
+// from 5.8-6.0 to 6.65 TB/s (same-box sweeps: update 14/12/10 per CU
+// 6.64/6.72/6.74 TB/s; fused 12/10/8 6.57/6.65/6.64, storing the gradient
+// 10/8 6.46/6.50).  The plain reduce (5 streams) and the gather (2) are
+// fastest without a cap.  The byte counts are multiples of 1 KiB and give the
+// same count under any allocation granularity up to 1 KiB.
+constexpr unsigned kAdamResidencyLds = 16 * 1024;        // 160 / 16 -> 10 workgroups
+constexpr unsigned kFusedResidencyLds = 16 * 1024;       // 160 / 16 -> 10 workgroups
+constexpr unsigned kFusedGradResidencyLds = 20 * 1024;   // 160 / 20 -> 8 workgroups
 // The reduce in accumulate mode (6 streams) and with FP32 contributions
 // (5 streams of 16-byte loads) are fastest with 64-lane workgroups capped at
 // 20 and 16 per CU: 6.14 -> 6.4 and 6.1 -> 6.4 TB/s on the 7B-layer shards.
@@ -666,7 +670,7 @@ template <int N, int WD, bool WG, bool ACC>
 hipError_t fused_vec_launch(const FusedParams& p, int n_shards, hipStream_t s) {
   dim3 grid(grid_x(p.shard >> 2, n_shards, kFusedBlock), n_shards);
   hipLaunchKernelGGL((fused_vec_kernel<N, WD, WG, ACC, kFusedBlock>), grid, dim3(kFusedBlock),
-                     kFusedResidencyLds, s, p);
+                     WG ? kFusedGradResidencyLds : kFusedResidencyLds, s, p);
   return hipGetLastError();
 }
 
