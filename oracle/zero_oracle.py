@@ -27,6 +27,13 @@ weight decay is decoupled and scaled by the learning rate; the reduction is
 w_0*x_0 + w_1*x_1 + ... summed left to right in rank order with every product
 and sum rounded separately; the partition is N contiguous equal slices of the
 zero-padded flat vector; BF16 rounding is round-to-nearest-even.
+
+Pins: every function here is checked by the CPU tests against values the
+pages print, closed forms, exact rational arithmetic or an independent
+library routine (see the tests named test_oracle_*).  Parity unpinned: the
+exact bits of multi-step AdamW states beyond what the closed forms fix rest
+on the readings above; the pins fix the formula, and a per-element scalar
+evaluation fixes the vectorised code.
 """
 from __future__ import annotations
 
