@@ -316,6 +316,10 @@ int zero_all_gather_layer(const void* const* shards, int n_shards, int64_t shard
  *   micro-batches 0..mb-1 only.
  * zero_offload_sync: waits for every queued copy and kernel of the handle; the
  *   host shard may be read after it returns.
+ * compute_stream may change from one call to the next: the handle orders its
+ * own copies and kernels on each slot by events.  Ordering the writes into
+ * slot_contrib after the kernel that last read that slot stays the caller's
+ * (automatic when both run on one stream).
  * Errors: ZERO_ERR_ARG / ZERO_ERR_ALIGN / ZERO_ERR_SIZE for bad arguments
  * (ZERO_ERR_SIZE also for more than ZERO_OFFLOAD_MAX_CHUNKS chunks: the handle
  * keeps two events per chunk, or when the handle's host memory cannot be

@@ -109,3 +109,73 @@ def test_offload_misuse_is_rejected():
     stage = [torch.zeros(chunk, device="cuda") for _ in range(2)]
     with pytest.raises(z.ZeroError, match="ZERO_ERR_SIZE"):
         z.zero_offload_create(4, host.numel(), chunk, host, slots, stage)
+
+
+@pytest.mark.parametrize("fuse_last_2", [False, True])
+def test_offload_compute_stream_changes_between_steps(fuse_last_2):
+    """Step 1 runs on stream A, its updates held back by a spin kernel; step 2
+    runs on stream B, whose contribution writes wait only for step 1's
+    reductions.  Step 2's first reductions write the staging slots that step
+    1's delayed updates still read, so the handle itself must order them.
+    Both steps are checked against the oracle (host accumulation, then the
+    state after t=1 and t=2)."""
+    if not hasattr(torch.cuda, "_sleep"):
+        pytest.skip("torch.cuda._sleep not available")
+    shard, chunk, n_ranks, n_micro = 4 * 4096 + 100, 4096, 4, 2
+    print(f"offload stream change shard={shard} chunk={chunk} fuse_last_2={fuse_last_2}", flush=True)
+    st = OffloadStep(shard, n_ranks, chunk, device="cuda")
+    g = S.rng(11)
+    contrib = [[[[S.bf16_normal(g, st.chunk_len(c), 1e-3) for _ in range(n_ranks)]
+                 for c in range(st.n_chunks)] for _ in range(n_micro)] for _ in range(2)]
+    pool = [[[[bf16_to_dev(x) for x in rc] for rc in mb] for mb in step] for step in contrib]
+    p0, m0, v0 = S.host_state(12, shard, 0.02)
+    st.master.copy_(torch.from_numpy(p0))
+    w = np.full(n_ranks, 1.0 / (n_ranks * n_micro), np.float32)
+    hps = [dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, step=t) for t in (1, 2)]
+    A, B = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def produce(step, mb, c):
+        for r, vw in enumerate(st.contrib_views(c)):
+            vw.copy_(pool[step][mb][c][r])
+
+    with torch.cuda.stream(A):
+        for mb in range(n_micro):
+            for c in range(st.n_chunks):
+                produce(0, mb, c)
+                st.engine.reduce(c, mb, w, stream=A)
+        reduced = torch.cuda.Event()
+        reduced.record(A)
+        for c in range(st.n_chunks):
+            torch.cuda._sleep(20_000_000)      # bounded spin: delays this update on A
+            st.engine.adam(c, st.master, st.exp_avg, st.exp_avg_sq, st.bf16, hps[0], stream=A)
+    with torch.cuda.stream(B):
+        B.wait_event(reduced)                  # the contribution slots are free after the reductions
+        for mb in range(n_micro):
+            last = fuse_last_2 and mb == n_micro - 1
+            for c in range(st.n_chunks):
+                produce(1, mb, c)
+                if last:
+                    st.engine.reduce_adam(c, mb, w, st.master, st.exp_avg, st.exp_avg_sq, st.bf16, hps[1],
+                                          stream=B)
+                else:
+                    st.engine.reduce(c, mb, w, stream=B)
+        if not fuse_last_2:
+            for c in range(st.n_chunks):
+                st.engine.adam(c, st.master, st.exp_avg, st.exp_avg_sq, st.bf16, hps[1], stream=B)
+    st.sync()
+    torch.cuda.synchronize()
+    host = st.host.numpy().copy()
+    sc = [oracle.adam_scalars(1e-3, 0.9, 0.999, 1e-8, 0.0, t) for t in (1, 2)]
+    for c in range(st.n_chunks):
+        lo, hi = c * chunk, c * chunk + st.chunk_len(c)
+        acc = [oracle.offload_accumulate([contrib[s][mb][c] for mb in range(n_micro)], w) for s in (0, 1)]
+        on_host = n_micro - 1 if fuse_last_2 else n_micro
+        assert_grad_exact(host[lo:hi], oracle.offload_accumulate([contrib[1][mb][c] for mb in range(on_host)], w),
+                          f"host chunk {c}")
+        p1, m1, v1, _ = oracle.adam_step(p0[lo:hi], m0[lo:hi], v0[lo:hi], acc[0], sc[0])
+        ref = oracle.adam_step(p1, m1, v1, acc[1], sc[1])
+        assert_state_close(f32_to_host(st.master[lo:hi]), f32_to_host(st.exp_avg[lo:hi]),
+                           f32_to_host(st.exp_avg_sq[lo:hi]), bf16_to_host(st.bf16[lo:hi]), ref,
+                           f"chunk {c}")
+    st.engine.close()

@@ -11,7 +11,10 @@
 //     - the H2D into staging[s] waits for the last D2H from it and the last
 //       kernel that used it;
 //     - a non-accumulating reduce into staging[s] waits for the last D2H from it;
-//     - the D2H from staging[s] waits for the reduce kernel that wrote it.
+//     - the D2H from staging[s] waits for the reduce kernel that wrote it;
+//     - every kernel on slot s waits for the previous one (directly, or
+//       through the H2D that it waits for), so kernel_done[s] covers all of
+//       them even when the caller changes compute streams between calls.
 //   host chunk c is written by its D2H and read by its H2D, so
 //     - an H2D of chunk c waits for the last D2H into chunk c;
 //     - a D2H into chunk c waits for the last H2D out of chunk c.
@@ -211,6 +214,7 @@ int zero_offload_stream(zero_offload* h, int op, int64_t chunk, int micro_batch,
       if (st) return st;
     } else {
       ZCHK(wait(cs, h->d2h_done[s]));
+      ZCHK(wait(cs, h->kernel_done[s]));   // an update still reading staging[s] on another stream
     }
     RsParams p;
     memset(&p, 0, sizeof p);
@@ -261,6 +265,10 @@ int zero_offload_stream(zero_offload* h, int op, int64_t chunk, int micro_batch,
     if (micro_batch > 0) {
       st = stream_in(h, chunk, s, len, cs);
       if (st) return st;
+    } else {
+      // staging[s] is not used, but kernel_done[s] is recorded again below:
+      // keep it after every earlier kernel on the slot, whatever its stream
+      ZCHK(wait(cs, h->kernel_done[s]));
     }
     FusedParams p;
     memset(&p, 0, sizeof p);
