@@ -62,7 +62,7 @@ def _chk32(a: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# a1: flatten, pad, partition
+# Flatten, pad, partition
 # ---------------------------------------------------------------------------
 def shard_layout(numels: Iterable[int], n_shards: int, align: int = SHARD_ALIGN):
     """Return (psi, psi_pad, shard_numel) for a unit made of tensors `numels`.
@@ -103,7 +103,7 @@ def shard_bounds(psi_pad: int, n_shards: int, k: int):
 
 
 # ---------------------------------------------------------------------------
-# a2: loss-normalisation weights
+# Loss-normalisation weights
 # ---------------------------------------------------------------------------
 def weights_mean(n_ranks: int) -> np.ndarray:
     """Equal weights 1/N: the batch-mean objective (slide, note 原 N48)."""
@@ -179,7 +179,7 @@ def _f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# a3: element-wise weighted reduction (all-reduce result) and reduce-scatter
+# Element-wise weighted reduction (all-reduce result) and reduce-scatter
 # ---------------------------------------------------------------------------
 def _contribution_f32(x: np.ndarray) -> np.ndarray:
     """A rank's contribution as float32: BF16 bit patterns are widened exactly;
@@ -238,7 +238,7 @@ def reduce_accumulate(acc: np.ndarray, rank_grads, weights) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# a4/a5: mixed-precision Adam owner update, BF16 working-weight pack
+# Mixed-precision Adam owner update, BF16 working-weight pack
 # ---------------------------------------------------------------------------
 def adam_scalars(lr, beta1, beta2, eps, weight_decay, step: int) -> dict:
     """Per-step scalars, formed once on the host.  The pages name only Adam's
@@ -303,7 +303,7 @@ def _adam_step(p, m, v, g, sc):
 
 
 # ---------------------------------------------------------------------------
-# a6: all-gather into a temporary full view
+# All-gather into a temporary full view
 # ---------------------------------------------------------------------------
 def all_gather(shards: Sequence[np.ndarray], psi: int | None = None) -> np.ndarray:
     """Every participant's full view is the concatenation of the owner shards
@@ -340,7 +340,7 @@ def sharded_step(rank_grads, weights, masters, exp_avgs, exp_avg_sqs, sc: dict):
 
 
 # ---------------------------------------------------------------------------
-# a8: host-offloaded gradient shard accumulated over micro-batches
+# Host-offloaded gradient shard accumulated over micro-batches
 # ---------------------------------------------------------------------------
 def offload_accumulate(per_micro_batch_grads: Sequence[Sequence[np.ndarray]], weights) -> np.ndarray:
     """The host gradient shard after M micro-batches (blog, section 分片放到
