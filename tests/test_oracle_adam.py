@@ -205,3 +205,38 @@ def test_clip_coefficient_closed_forms():
     # scaling by 1 or a power of two is exact
     assert np.array_equal(oracle.scale_grad(g, np.float32(1.0)), g)
     assert np.array_equal(oracle.scale_grad(g, np.float32(0.25)), g / np.float32(4))
+
+
+@pytest.mark.parametrize("steps", [3, 20])
+def test_constant_gradient_adamw_is_an_affine_recurrence(steps):
+    # AdamW with a constant g: the moments do not see the decay, so m_hat = g
+    # and v_hat = g^2 at every step as above, and p follows
+    #   p_t = a*p_{t-1} - c,  a = 1 - lr*wd,  c = lr*g/(|g|+eps)
+    # whose solution is p_T = a^T p_0 - c (1 - a^T)/(1 - a).  Also
+    # m_T = (1 - b1^T) g and v_T = (1 - b2^T) g^2.  Hyper-parameters of the
+    # 7B-class layer's AdamW (lr 1e-3, wd 0.1), t = 1..T.
+    p, m, v, g = _state(7, g_sigma=1e-2)
+    p0 = _f64(p)
+    for t in range(1, steps + 1):
+        p, m, v, _ = oracle.adam_step(p, m, v, g, _sc(t, weight_decay=0.1))
+    lr, wd, eps = float(np.float32(1e-3)), float(np.float32(0.1)), float(np.float32(1e-8))
+    b1, b2 = float(np.float32(0.9)), float(np.float32(0.999))
+    gd = _f64(g)
+    a = 1.0 - lr * wd
+    c = lr * gd / (np.abs(gd) + eps)
+    expected = a ** steps * p0 - c * (1 - a ** steps) / (1 - a)
+    # each step: the update direction carries about 4t roundings (the moments'
+    # t-step recurrences) plus a dozen in the step itself, relative to lr; the
+    # decay product and the final subtraction add 3 roundings of |p|; a <= 1
+    # keeps earlier errors from growing
+    pmax = np.abs(p0) + steps * np.abs(c)
+    bound = steps * ((4 * steps + 14) * U * lr + 3 * U * pmax)
+    assert np.all(np.abs(_f64(p) - expected) <= bound)
+    assert np.all(np.abs(_f64(m) - (1 - b1 ** steps) * gd) <= 3 * steps * U * np.abs(gd))
+    assert np.all(np.abs(_f64(v) - (1 - b2 ** steps) * gd * gd) <= 4 * steps * U * gd * gd)
+    # the decay is visible: where the closed forms with and without decay
+    # are far apart, the oracle is far from the one without
+    no_decay = p0 - steps * c
+    apart = np.abs(expected - no_decay) > 10 * bound
+    assert apart.mean() > 0.5
+    assert np.all(np.abs(_f64(p) - no_decay)[apart] > bound[apart])

@@ -1,6 +1,9 @@
 """Plants plausible mistakes in a copy of the oracle, on the CPU, and checks that
 the oracle's pins (not the scalar brute force, which restates the formulas)
-catch every one of them."""
+catch every one of them.  The pins run in a scratch tree holding the copy, the
+tests and the input generators only; a control run on the unmodified copy must
+pass there, and a planted mistake counts as caught only when a pin fails (an
+error in collection or set-up does not count)."""
 import os
 import shutil
 import subprocess
@@ -53,9 +56,17 @@ MUTATIONS = {
                          "    m1 ="),
     "bf16_packed_from_old_master": ("return p1, m1, v1, f32_to_bf16_rne(p1)", "return p1, m1, v1, f32_to_bf16_rne(p)"),
     "mean_weight_off": ("[float(1) / float(n_ranks)]", "[float(1) / float(n_ranks + 1)]"),
+    "decay_also_on_first_moment": ('m1 = _chk32(_chk32(sc["beta1"] * m) + _chk32(sc["one_minus_beta1"] * g))',
+                                   'm1 = _chk32(_chk32(_chk32(sc["beta1"] * m) + _chk32(sc["one_minus_beta1"] * g))'
+                                   ' - _chk32(_chk32(sc["lr"] * sc["weight_decay"]) * m))'),
     "accumulate_mode_drops_acc": ("return _chk32(acc + reduce_full(rank_grads, weights))",
                                   "return _chk32(reduce_full(rank_grads, weights))"),
 }
+
+
+# the pin files; the scalar brute force restates the formulas, so it is left out
+PIN_FILES = ["tests/test_oracle_adam.py", "tests/test_oracle_invariants.py",
+             "tests/test_oracle_ledger_layout.py", "tests/test_oracle_reduce_bf16.py"]
 
 
 @pytest.fixture(scope="module")
@@ -64,17 +75,28 @@ def oracle_src():
         return f.read()
 
 
+def _run_pins(tmp_path, src):
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle",
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    (tmp_path / "oracle" / "zero_oracle.py").write_text(src)
+    for d in ("tests", "synthetic"):
+        os.symlink(os.path.join(ROOT, d), tmp_path / d)
+    return subprocess.run(
+        [sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", *PIN_FILES,
+         "-m", "not gpu", "-k", "not brute"],
+        cwd=tmp_path, capture_output=True, text=True, timeout=300)
+
+
+def test_pins_pass_on_the_unmodified_oracle(oracle_src, tmp_path):
+    r = _run_pins(tmp_path, oracle_src)
+    assert r.returncode == 0, f"the pins fail on the unmodified copy:\n{r.stdout[-2000:]}"
+
+
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_pins_catch_planted_mistake(name, oracle_src, tmp_path):
     old, new = MUTATIONS[name]
     assert old in oracle_src, f"mutation anchor for {name} no longer in the oracle"
-    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle",
-                    ignore=shutil.ignore_patterns("__pycache__"))
-    (tmp_path / "oracle" / "zero_oracle.py").write_text(oracle_src.replace(old, new, 1))
-    for d in ("tests", "synthetic"):
-        os.symlink(os.path.join(ROOT, d), tmp_path / d)
-    r = subprocess.run(
-        [sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", "tests",
-         "-m", "not gpu", "-k", "oracle and not brute and not mutations"],
-        cwd=tmp_path, capture_output=True, text=True, timeout=300)
-    assert r.returncode == 1, f"planted mistake {name} was not caught:\n{r.stdout[-2000:]}"
+    r = _run_pins(tmp_path, oracle_src.replace(old, new, 1))
+    last = r.stdout.strip().splitlines()[-1] if r.stdout.strip() else ""
+    assert r.returncode == 1 and " failed" in last and " error" not in last, \
+        f"planted mistake {name} was not caught by a failing pin:\n{r.stdout[-2000:]}"
