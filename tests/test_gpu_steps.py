@@ -145,8 +145,8 @@ def test_layer7b_clipped_step():
     # the step with the global-norm clip at the full 7B-class layer size, in the
     # launch configuration the benchmark times: the norm against the oracle's
     # FP64 sum (different summation order: relative 1e-12), the coefficient
-    # within 1 ulp, and the scaled update bit-exact on windows given the
-    # device's coefficient (both sides then take the same clip decision)
+    # equal to the oracle's, and the scaled update on windows against the
+    # oracle's Adam on the gradient scaled by the oracle's own coefficient
     from zero_sharded_optimizer_reduce_amd import _lib
     wl = S.WORKLOADS["layer7b_weighted_adamw"]
     n, psi = wl.n_ranks, wl.psi
@@ -179,9 +179,12 @@ def test_layer7b_clipped_step():
     ref_nsq = oracle.grad_norm_sq([red])
     got_nsq = float(norm_sq.item())
     assert abs(got_nsq - ref_nsq) <= 1e-12 * ref_nsq, (got_nsq, ref_nsq)
+    # the two FP64 sums agree to about 1e-16 relative; rounded to FP32 the
+    # coefficients could differ only if they fell on either side of a rounding
+    # boundary (odds about 1e-9), and the seeded inputs fix which case holds
     ref_c = oracle.clip_coefficient(ref_nsq, max_norm)
     got_c = np.float32(coef.item())
-    assert ref_c < 1 and abs(int(got_c.view(np.int32)) - int(ref_c.view(np.int32))) <= 1, (got_c, ref_c)
+    assert ref_c < 1 and got_c == ref_c, (got_c, ref_c)
     gp = np.concatenate([f32_to_host(x) for x in st.master])
     gm = np.concatenate([f32_to_host(x) for x in st.exp_avg])
     gv = np.concatenate([f32_to_host(x) for x in st.exp_avg_sq])
@@ -189,7 +192,7 @@ def test_layer7b_clipped_step():
     sc = _sc(hp)
     width = 4096
     for a in _windows(psi, n, st.shard, np.random.default_rng(wl.seed + 40)):
-        g_ref = oracle.scale_grad(red[a:a + width], got_c)
+        g_ref = oracle.scale_grad(red[a:a + width], ref_c)
         z0 = np.zeros(width, np.float32)
         ref = oracle.adam_step(f32_to_host(master0[a:a + width]), z0, z0.copy(), g_ref, sc)
         assert_state_close(gp[a:a + width], gm[a:a + width], gv[a:a + width], gb[a:a + width], ref,
