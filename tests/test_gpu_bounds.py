@@ -17,7 +17,7 @@ from gpu_helpers import (assert_grad_exact, assert_state_close, bf16_to_dev, bf1
 
 pytestmark = pytest.mark.gpu
 
-z = pytest.importorskip("zero_sharded_optimizer_reduce_amd")
+import zero_sharded_optimizer_reduce_amd as z  # noqa: E402  (a broken package must fail, not skip)
 
 SENTINEL = {torch.float32: 0x7FBADBAD, torch.bfloat16: 0x7FBD, torch.uint8: 0xA5}   # NaN payloads / a byte
 INT_VIEW = {torch.float32: torch.int32, torch.bfloat16: torch.int16, torch.uint8: torch.uint8}

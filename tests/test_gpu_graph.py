@@ -25,7 +25,7 @@ from gpu_helpers import f32_to_dev
 
 pytestmark = pytest.mark.gpu
 
-z = pytest.importorskip("zero_sharded_optimizer_reduce_amd")
+import zero_sharded_optimizer_reduce_amd as z  # noqa: E402  (a broken package must fail, not skip)
 from zero_sharded_optimizer_reduce_amd import _lib  # noqa: E402
 from zero_sharded_optimizer_reduce_amd.drivers import GraphedStep, ShardedStep  # noqa: E402
 

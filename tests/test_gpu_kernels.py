@@ -13,7 +13,7 @@ from gpu_helpers import (assert_grad_exact, assert_state_close, bf16_to_dev, bf1
 
 pytestmark = pytest.mark.gpu
 
-z = pytest.importorskip("zero_sharded_optimizer_reduce_amd")
+import zero_sharded_optimizer_reduce_amd as z  # noqa: E402  (a broken package must fail, not skip)
 
 
 def _sc(hp):

@@ -16,7 +16,7 @@ from gpu_helpers import assert_grad_exact, assert_state_close, bf16_to_host, f32
 
 pytestmark = pytest.mark.gpu
 
-z = pytest.importorskip("zero_sharded_optimizer_reduce_amd")
+import zero_sharded_optimizer_reduce_amd as z  # noqa: E402  (a broken package must fail, not skip)
 
 W = 4096
 

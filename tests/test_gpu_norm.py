@@ -15,7 +15,7 @@ from gpu_helpers import assert_state_close, bf16_to_host, f32_to_dev, f32_to_hos
 
 pytestmark = pytest.mark.gpu
 
-z = pytest.importorskip("zero_sharded_optimizer_reduce_amd")
+import zero_sharded_optimizer_reduce_amd as z  # noqa: E402  (a broken package must fail, not skip)
 
 NORM_RTOL = 1e-12      # FP64 sums of up to 2^28 exact squares: error << 1e-12 relative
 

@@ -15,7 +15,7 @@ from gpu_helpers import assert_grad_exact, assert_state_close, bf16_to_dev, bf16
 
 pytestmark = pytest.mark.gpu
 
-z = pytest.importorskip("zero_sharded_optimizer_reduce_amd")
+import zero_sharded_optimizer_reduce_amd as z  # noqa: E402  (a broken package must fail, not skip)
 from zero_sharded_optimizer_reduce_amd import _lib  # noqa: E402
 from zero_sharded_optimizer_reduce_amd.drivers import OffloadStep  # noqa: E402
 

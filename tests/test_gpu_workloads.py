@@ -25,7 +25,7 @@ from synthetic.workloads import BUCKET, CHAIN_8B, OFFLOAD_8B, OWNER_8B
 
 pytestmark = pytest.mark.gpu
 
-z = pytest.importorskip("zero_sharded_optimizer_reduce_amd")
+import zero_sharded_optimizer_reduce_amd as z  # noqa: E402  (a broken package must fail, not skip)
 from zero_sharded_optimizer_reduce_amd.drivers import BucketedOwnerStep, OffloadStep, Zero3Chain  # noqa: E402
 
 W = 1 << 16     # window width
