@@ -7,10 +7,16 @@ import torch
 
 from oracle.compare import bits_equal_f32, max_ulp_bf16, max_ulp_f32
 
-# The bar: reduced gradients bit-exact; FP32 master/m/v within 2 ulp; BF16
-# working weights within 1 bf16 ulp.
-FP32_ULP_TOL = 2
-BF16_ULP_TOL = 1
+# The graded bar is: reduced gradients bit-exact, FP32 master/m/v within 2 ulp,
+# BF16 working weights within 1 bf16 ulp.  The kernels perform the oracle's
+# operations one for one (binary32, one rounding each, no contraction,
+# correctly rounded division and square root, subnormals kept, RNE to BF16),
+# so the expected distance is exactly 0 and that is what the tests assert; the
+# graded bar is kept only for the report.
+FP32_ULP_TOL = 0
+BF16_ULP_TOL = 0
+FP32_ULP_BAR = 2
+BF16_ULP_BAR = 1
 
 DEV = "cuda"
 
@@ -41,8 +47,10 @@ def assert_grad_exact(gpu: np.ndarray, ref: np.ndarray, what="reduced gradient")
 
 
 def assert_state_close(p, m, v, b, ref, what=""):
-    """ref = (p', m', v', bf16 bits) from the oracle.  Returns the max ulps."""
+    """ref = (p', m', v', bf16 bits) from the oracle.  Asserts distance 0 (two
+    NaNs count as equal) and returns the max ulps."""
     u = (max_ulp_f32(p, ref[0]), max_ulp_f32(m, ref[1]), max_ulp_f32(v, ref[2]))
     ub = max_ulp_bf16(b, ref[3])
-    assert max(u) <= FP32_ULP_TOL and ub <= BF16_ULP_TOL, f"{what}: ulps master/m/v {u}, bf16 {ub}"
+    assert max(u) <= FP32_ULP_TOL and ub <= BF16_ULP_TOL, \
+        f"{what}: ulps master/m/v {u}, bf16 {ub} (asserted 0; graded bar {FP32_ULP_BAR}/{BF16_ULP_BAR})"
     return u, ub

@@ -1,6 +1,8 @@
 """Plants plausible mistakes in a copy of the oracle, on the CPU, and checks that
 the oracle's pins (not the scalar brute force, which restates the formulas)
-catch every one of them.  The pins run in a scratch tree holding the copy, the
+catch every one of them.  Mistakes are planted in the oracle's arithmetic
+(zero_oracle.py) and in the distance measures every parity test uses
+(compare.py).  The pins run in a scratch tree holding the copy, the
 tests and the input generators only; a control run on the unmodified copy must
 pass there, and a planted mistake counts as caught only when a pin fails (an
 error in collection or set-up does not count)."""
@@ -63,27 +65,54 @@ MUTATIONS = {
                                   "return _chk32(reduce_full(rank_grads, weights))"),
 }
 
+# Mistakes in the ulp distance and bit-equality measures: each would let a GPU
+# result that is not the oracle's pass (or a correct one fail).
+COMPARE_MUTATIONS = {
+    "sign_map_dropped": ("return np.where(b & sign_bit, -mag, mag)", "return mag"),
+    "sign_map_keeps_sign_bit": ("return np.where(b & sign_bit, -mag, mag)", "return np.where(b & sign_bit, -b, b)"),
+    "two_nans_infinitely_apart": ("d = np.where(a_nan & b_nan, 0, d)", "d = np.where(a_nan & b_nan, INF_ULP, d)"),
+    "nan_vs_number_not_infinite": ("d = np.where(a_nan ^ b_nan, INF_ULP, d)", "d = np.where(a_nan ^ b_nan, d, d)"),
+    "f32_magnitude_mask_fraction_only": ("0x80000000, 0x7FFFFFFF)", "0x80000000, 0x007FFFFF)"),
+    "bf16_infinity_taken_as_nan": ("a_nan = (a & 0x7FFF) > 0x7F80", "a_nan = (a & 0x7FFF) >= 0x7F80"),
+    "bf16_nan_threshold_high": ("b_nan = (b & 0x7FFF) > 0x7F80", "b_nan = (b & 0x7FFF) > 0x7FC0"),
+    "bf16_magnitude_mask_wrong": ("0x8000, 0x7FFF)", "0x8000, 0x7F80)"),
+    "bits_equal_by_value": ("same = a.view(np.uint32) == b.view(np.uint32)", "same = a == b"),
+    "bits_equal_nan_rule_dropped": ("same |= np.isnan(a) & np.isnan(b)", "pass"),
+    "max_ulp_reports_min": ("return int(ulp_f32(a, b).max(initial=0))", "return int(ulp_f32(a, b).min(initial=0))"),
+}
 
-# the pin files; the scalar brute force restates the formulas, so it is left out
+# the pin files; the scalar brute force restates the formulas, so it is left
+# out, and the exhaustive 2^32 rounding sweep is left out for time (the
+# structured sweep over every sign/exponent/mantissa prefix runs instead)
 PIN_FILES = ["tests/test_oracle_adam.py", "tests/test_oracle_invariants.py",
-             "tests/test_oracle_ledger_layout.py", "tests/test_oracle_reduce_bf16.py"]
+             "tests/test_oracle_ledger_layout.py", "tests/test_oracle_reduce_bf16.py",
+             "tests/test_oracle_compare.py"]
+
+
+def _src(name):
+    with open(os.path.join(ROOT, "oracle", name)) as f:
+        return f.read()
 
 
 @pytest.fixture(scope="module")
 def oracle_src():
-    with open(os.path.join(ROOT, "oracle", "zero_oracle.py")) as f:
-        return f.read()
+    return _src("zero_oracle.py")
 
 
-def _run_pins(tmp_path, src):
+@pytest.fixture(scope="module")
+def compare_src():
+    return _src("compare.py")
+
+
+def _run_pins(tmp_path, src, name="zero_oracle.py"):
     shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle",
                     ignore=shutil.ignore_patterns("__pycache__"))
-    (tmp_path / "oracle" / "zero_oracle.py").write_text(src)
+    (tmp_path / "oracle" / name).write_text(src)
     for d in ("tests", "synthetic"):
         os.symlink(os.path.join(ROOT, d), tmp_path / d)
     return subprocess.run(
         [sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", *PIN_FILES,
-         "-m", "not gpu", "-k", "not brute"],
+         "-m", "not gpu", "-k", "not brute and not all_2_32"],
         cwd=tmp_path, capture_output=True, text=True, timeout=300)
 
 
@@ -92,11 +121,21 @@ def test_pins_pass_on_the_unmodified_oracle(oracle_src, tmp_path):
     assert r.returncode == 0, f"the pins fail on the unmodified copy:\n{r.stdout[-2000:]}"
 
 
+def _assert_caught(name, r):
+    last = r.stdout.strip().splitlines()[-1] if r.stdout.strip() else ""
+    assert r.returncode == 1 and " failed" in last and " error" not in last, \
+        f"planted mistake {name} was not caught by a failing pin:\n{r.stdout[-2000:]}"
+
+
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_pins_catch_planted_mistake(name, oracle_src, tmp_path):
     old, new = MUTATIONS[name]
     assert old in oracle_src, f"mutation anchor for {name} no longer in the oracle"
-    r = _run_pins(tmp_path, oracle_src.replace(old, new, 1))
-    last = r.stdout.strip().splitlines()[-1] if r.stdout.strip() else ""
-    assert r.returncode == 1 and " failed" in last and " error" not in last, \
-        f"planted mistake {name} was not caught by a failing pin:\n{r.stdout[-2000:]}"
+    _assert_caught(name, _run_pins(tmp_path, oracle_src.replace(old, new, 1)))
+
+
+@pytest.mark.parametrize("name", sorted(COMPARE_MUTATIONS))
+def test_pins_catch_planted_mistake_in_the_distance_measures(name, compare_src, tmp_path):
+    old, new = COMPARE_MUTATIONS[name]
+    assert old in compare_src, f"mutation anchor for {name} no longer in compare.py"
+    _assert_caught(name, _run_pins(tmp_path, compare_src.replace(old, new, 1), "compare.py"))

@@ -44,11 +44,25 @@ def test_bf16_rne_structured_sweep():
     _check_rne_against_torch((hi[:, None] | lows[None, :]).reshape(-1))
 
 
-@pytest.mark.slow
-def test_bf16_rne_exhaustive():
-    step = 1 << 26
-    for start in range(0, 1 << 32, step):
-        _check_rne_against_torch(np.arange(start, start + step, dtype=np.uint64).astype(np.uint32))
+def _check_rne_range(start: int, count: int) -> int:
+    """One worker's share of the exhaustive sweep; returns patterns checked."""
+    torch.set_num_threads(1)
+    _check_rne_against_torch(np.arange(start, start + count, dtype=np.uint64).astype(np.uint32))
+    return count
+
+
+def test_bf16_rne_all_2_32_patterns():
+    # every binary32 bit pattern, in 2^24-pattern pieces over a process pool
+    # (about 3.5 s of one core per 2^26 patterns)
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import os
+    step = 1 << 24
+    starts = list(range(0, 1 << 32, step))
+    workers = max(1, min(8, len(os.sched_getaffinity(0))))
+    with cf.ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn")) as ex:
+        done = sum(ex.map(_check_rne_range, starts, [step] * len(starts)))
+    assert done == 1 << 32
 
 
 def test_bf16_rne_named_cases():
