@@ -323,8 +323,10 @@ int zero_all_gather_layer(const void* const* shards, int n_shards, int64_t shard
  * Errors: ZERO_ERR_ARG / ZERO_ERR_ALIGN / ZERO_ERR_SIZE for bad arguments
  * (ZERO_ERR_SIZE also for more than ZERO_OFFLOAD_MAX_CHUNKS chunks: the handle
  * keeps two events per chunk, or when the handle's host memory cannot be
- * allocated), ZERO_ERR_STATE for a chunk out of range, a REDUCE with mb > 0 for a chunk
- * that has no earlier micro-batch, or an ADAM for a chunk never reduced;
+ * allocated), ZERO_ERR_STATE for a chunk out of range, a REDUCE or REDUCE_ADAM
+ * with mb > 0 whose micro-batch mb - 1 is not the chunk's last one, or an ADAM
+ * for a chunk with no accumulation: never reduced, or already consumed by an
+ * ADAM or REDUCE_ADAM (after which the chunk starts again at mb 0);
  * ZERO_ERR_HIP on runtime failures. */
 typedef struct zero_offload zero_offload;
 enum { ZERO_OFFLOAD_REDUCE = 0, ZERO_OFFLOAD_ADAM = 1, ZERO_OFFLOAD_REDUCE_ADAM = 2 };

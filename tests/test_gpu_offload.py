@@ -100,6 +100,18 @@ def test_offload_misuse_is_rejected():
     with pytest.raises(z.ZeroError, match="ZERO_ERR_STATE"):
         st.engine.reduce(4, 0, w)                 # chunk out of range
     st.engine.reduce(0, 0, w)
+    st.engine.reduce(0, 1, w)
+    st.engine.adam(0, st.master, st.exp_avg, st.exp_avg_sq, st.bf16, hp)
+    # the update consumed chunk 0's accumulation: neither a further micro-batch
+    # onto it nor a second update may follow; a new accumulation starts at 0
+    with pytest.raises(z.ZeroError, match="ZERO_ERR_STATE"):
+        st.engine.reduce(0, 2, w)
+    with pytest.raises(z.ZeroError, match="ZERO_ERR_STATE"):
+        st.engine.adam(0, st.master, st.exp_avg, st.exp_avg_sq, st.bf16, hp)
+    st.engine.reduce_adam(1, 0, w, st.master, st.exp_avg, st.exp_avg_sq, st.bf16, hp)
+    with pytest.raises(z.ZeroError, match="ZERO_ERR_STATE"):
+        st.engine.reduce(1, 1, w)
+    st.engine.reduce(0, 0, w)
     st.sync()
     st.engine.close()
     # more chunks than a handle may hold (two events per chunk)

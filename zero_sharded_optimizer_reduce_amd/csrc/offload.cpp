@@ -318,6 +318,7 @@ int zero_offload_stream(zero_offload* h, int op, int64_t chunk, int micro_batch,
   set_path(vec);
   ZCHK(launch_adam(a, vec, cs));
   ZCHK(record(h->kernel_done[s], cs));
+  h->last_mb[chunk] = -1;   // the accumulation of this chunk is consumed, as after REDUCE_ADAM
   return ZERO_OK;
 }
 
