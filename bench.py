@@ -3,22 +3,27 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the whole hot path over one batch of synthetic input.
-The default workload is one 7B-class transformer layer (d=4096, ffn=11008,
-202,375,168 parameters, N=4 ranks weighted by token counts 4096/3072/4096/2048,
-AdamW wd=0.1): reduce-scatter of the 4 ranks' BF16 gradients into 4 FP32 owner
-shards (one launch), the fused Adam/AdamW update of each owner shard (4
-launches) and the all-gather of the 4 BF16 working shards into the full view
-(one launch).  Inputs are resident in HBM before the timed region.
+The default workload is the largest one that fits one GPU: the ZeRO-3
+per-unit chain of an 8B Llama-like model (34 units: embedding, 32 layers with
+d=4096, ffn=14336, GQA kv_dim=1024, lm_head 128256x4096; 8,029,995,008
+parameters) with N=4 simulated ranks.  Forward: every unit's 4 BF16 owner
+shards are all-gathered into a temporary view, which is released.  Backward,
+units in reverse order: reduce-scatter of the 4 ranks' BF16 contributions
+into 4 FP32 owner shards, then the 4 owners' fused Adam updates (FP32 master,
+m, v and the BF16 working shard).  Inputs are resident in HBM before the timed
+region.  After the chain's buffers are released the same line carries the
+7B-class layer figures (d=4096, ffn=11008, 202,375,168 parameters, ranks
+weighted by token counts, AdamW wd=0.1) under an extra key.
 
-Other workloads (--workload): tiny_flat_1m, owner_share_8b_buckets (one
-owner's 2.0e9-parameter share in 64M buckets), zero3_chain_llama8b (34-unit
-gather/scatter chain of an 8B Llama-like model), offload_owner_8b_two_slots
-(host-offloaded gradient shard through two device slots).
+Other workloads (--workload): tiny_flat_1m, layer7b_weighted_adamw,
+owner_share_8b_buckets (one owner's 2.0e9-parameter share in 64M buckets),
+offload_owner_8b_two_slots (host-offloaded gradient shard through two device
+slots), copy_calibration (copies of known size for the byte counters).
 
 Prints ONE JSON line: params updated per second (value), the step time, the
 achieved algorithmic HBM bandwidth, the roofline entry of the dominant kernel
-measured with HIP events on the launch stream, and (default workload) the CPU
-oracle timed on a bounded sample of the same workload.
+measured with HIP events on the launch stream inside the timed region, and
+the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -28,6 +33,7 @@ import gc
 import hashlib
 import json
 import os
+import struct
 import sys
 import time
 
@@ -36,7 +42,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X published peak HBM3E bandwidth
-KERNEL_SRC = os.path.join(ROOT, "zero_sharded_optimizer_reduce_amd", "csrc", "kernels.hip")
+LIBZERO = os.path.join(ROOT, "zero_sharded_optimizer_reduce_amd", "libzero.so")
 PROFILES = os.path.join(ROOT, "profiles")
 METRIC = "params updated/sec per step and achieved HBM GB/s (% of MI355X peak), N=4"
 
@@ -47,40 +53,74 @@ B_ADAM = 30                     # read g, p, m, v (16 B); write p, m, v (12 B) +
 B_AG = 4                        # read and write one BF16 value
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def _elf_section(path: str, name: str) -> bytes:
+    """The bytes of section `name` of a little-endian ELF64 file."""
+    with open(path, "rb") as f:
+        d = f.read()
+    if d[:4] != b"\x7fELF" or d[4] != 2:
+        raise ValueError(f"{path} is not an ELF64 file")
+    shoff, = struct.unpack_from("<Q", d, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", d, 0x3A)
+
+    def header(i):
+        nm, _typ, _flags, _addr, off, size = struct.unpack_from("<IIQQQQ", d, shoff + i * shentsize)
+        return nm, off, size
+
+    strtab = header(shstrndx)[1]
+    for i in range(shnum):
+        nm, off, size = header(i)
+        if d[strtab + nm: d.index(b"\0", strtab + nm)] == name.encode():
+            return d[off:off + size]
+    raise ValueError(f"{path} has no {name} section")
+
+
+def device_code_hash() -> str:
+    """sha256 of the device code that libzero.so carries (its .hip_fatbin
+    section: every gfx950 code object of the library).  Builds are
+    deterministic and edits that leave the machine code alone (comments,
+    host code) keep the hash, so a stored counter reading stays valid exactly
+    as long as the kernels it measured are the ones that run."""
+    return hashlib.sha256(_elf_section(LIBZERO, ".hip_fatbin")).hexdigest()
 
 
 def _traffic(kernel: str, workload: str, launch_params: int):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None if there is none or the kernel source changed since."""
-    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.txt")
+    """(HBM bytes per launch, source note) of `kernel` from the committed
+    rocprofv3 counter summary, or (None, reason) if there is none, or the
+    kernel sources changed since it was taken, or it covers another size."""
+    name = f"{kernel}_{workload}_traffic.txt"
+    path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
-        return None
+        return None, f"no counter summary profiles/{name}"
     kv = {}
     for line in open(path):
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
-        return None
+    try:
+        code = device_code_hash()
+    except (OSError, ValueError) as e:
+        return None, f"device code of libzero.so not readable ({e})"
+    if kv.get("device_code_sha256") != code:
+        return None, f"profiles/{name} was taken on other device code"
     try:
         if int(kv["params_per_launch"]) != launch_params:
-            return None
-        return float(kv["hbm_bytes_per_launch"])
+            return None, f"profiles/{name} covers another launch size"
+        return float(kv["hbm_bytes_per_launch"]), (
+            f"profiles/{name}: FETCH_SIZE and WRITE_SIZE from two earlier rocprofv3 counter runs on "
+            f"this device code (sha256 {code[:12]}), not from this run")
     except (KeyError, ValueError):
-        return None
+        return None, f"profiles/{name} is incomplete"
 
 
-def _roofline(kernel, workload, ms, params):
+def _roofline(kernel, workload, ms, params, timing):
     achieved = B_ADAM * params / (ms * 1e-3) / 1e9
-    traffic = _traffic(kernel, workload, params)
+    traffic, source = _traffic(kernel, workload, params)
     return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+            "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "traffic_source": source,
             # the counters' bytes over the same measured launch time
             "traffic_gbs": None if traffic is None else traffic / (ms * 1e-3) / 1e9,
-            "kernel": kernel, "algorithmic_bytes_per_launch": B_ADAM * params}
+            "kernel": kernel, "params_per_launch": params, "algorithmic_bytes_per_launch": B_ADAM * params,
+            "launch_ms": ms, "timing": timing}
 
 
 @contextlib.contextmanager
@@ -132,6 +172,33 @@ class Timer:
         return float(sum(a.elapsed_time(b) for a, b in self.spans.get(name, [])))
 
 
+def event_overhead_ms(T, fn, reps=20, rounds=3):
+    """GPU time that one event recorded between two kernels adds to the
+    stream: reps back-to-back calls of fn timed with no event between them,
+    then with an event after every call; the difference over reps, median of
+    `rounds` alternations.  Spans taken between events inside a step carry
+    one such gap each, which the breakdowns subtract."""
+    torch = T.torch
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    est = []
+    with no_gc():
+        for _ in range(rounds):
+            a = T.ev()
+            for _ in range(reps):
+                fn()
+            b = T.ev()
+            c = T.ev()
+            for _ in range(reps):
+                fn()
+                d = T.ev()
+            torch.cuda.synchronize()
+            est.append((c.elapsed_time(d) - a.elapsed_time(b)) / reps)
+    est.sort()
+    return max(0.0, est[len(est) // 2])
+
+
 def copy_ceiling_gbs(nbytes=1 << 30, reps=20):
     """Same-run ceiling: the library's copy kernel (all-gather of one shard)
     over nbytes, read + write bytes per second."""
@@ -166,50 +233,76 @@ def _base(workload_desc, value, ms_step, args, extra_cfg=None):
 CPU_SLICE = 1 << 22
 
 
-def _cpu_slice_worker(slice_index: int, target_s: float):
-    """One process: the oracle's sharded step on one 2^22-parameter slice of the
-    7B-class layer workload, repeated until target_s seconds have passed.
-    Returns (parameters stepped, seconds)."""
+def _cpu_slice_inputs(kind: str, slice_index: int):
+    """Inputs of one 2^22-parameter slice of a workload, drawn on the host as
+    that workload draws them, and the oracle's weights and step scalars."""
     import oracle
     import synthetic as S
-    from synthetic.workloads import LAYER_7B as wl
+    from synthetic.workloads import CHAIN_8B, LAYER_7B
 
-    n, chunk = wl.n_ranks, CPU_SLICE
-    seed = wl.seed + 1000 * slice_index
-    grads = S.host_rank_grads(seed, n, chunk, wl.grad_sigma, S.rank_scales(wl.seed, n))
-    p, m, v = S.host_state(seed + 1, chunk, wl.master_sigma)
-    w = oracle.weights_from_counts(wl.extra["token_counts"])
+    if kind == "layer7b_weighted_adamw":
+        wl = LAYER_7B
+        seed = wl.seed + 1000 * slice_index
+        grads = S.host_rank_grads(seed, wl.n_ranks, CPU_SLICE, wl.grad_sigma, S.rank_scales(wl.seed, wl.n_ranks))
+        w = oracle.weights_from_counts(wl.extra["token_counts"])
+    else:   # zero3_chain_llama8b: slices of the embedding unit and of layer 0 in turn
+        wl = CHAIN_8B
+        seed = wl.seed + 1000 * slice_index + (0 if slice_index % 2 == 0 else 1)
+        grads = S.host_rank_grads(seed, wl.n_ranks, CPU_SLICE, wl.grad_sigma)
+        w = oracle.weights_mean(wl.n_ranks)
+    p, m, v = S.host_state(seed + 1, CPU_SLICE, wl.master_sigma)
     sc = oracle.adam_scalars(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay, 1)
-    s = chunk // n
+    return wl.n_ranks, grads, w, (p, m, v), sc
+
+
+def _cpu_slice_worker(kind: str, slice_index: int, target_s: float):
+    """One process: the oracle's sharded step (reduce-scatter, the N owners'
+    updates with the BF16 pack, all-gather) on one 2^22-parameter slice of the
+    workload, repeated until target_s seconds have passed.  Returns
+    (parameters stepped, seconds)."""
+    import oracle
+
+    n, grads, w, (p, m, v), sc = _cpu_slice_inputs(kind, slice_index)
+    s = CPU_SLICE // n
     done = 0
     t0 = time.perf_counter()
     while True:
         oracle.sharded_step(grads, w, [p[k * s:(k + 1) * s] for k in range(n)],
                             [m[k * s:(k + 1) * s] for k in range(n)],
                             [v[k * s:(k + 1) * s] for k in range(n)], sc)
-        done += chunk
+        done += CPU_SLICE
         el = time.perf_counter() - t0
         if el >= target_s:
             return done, el
 
 
-def cpu_baseline(target_s: float):
-    """The oracle, as it stands, on 2^22-parameter slices of the 7B-class layer
-    workload (reduce-scatter of 4 count-weighted BF16 ranks, AdamW, BF16 pack,
-    gather): first in this process on one thread for target_s seconds, then
-    in one process per available core (at most 16), each on its own slice,
-    for target_s seconds.  The slices are independent, as the shards are.
-    Runs before the GPU is touched."""
+CPU_SAMPLES = {
+    "layer7b_weighted_adamw": ("2^22-param slices of the 7B-class layer (4 count-weighted BF16 ranks, AdamW "
+                               "wd=0.1)", 202_375_168),
+    "zero3_chain_llama8b": ("2^22-param slices cut alternately from the embedding unit and from layer 0 of the "
+                            "8B chain (4 mean-weighted BF16 ranks, Adam t=1, wd=0)", 8_029_995_008),
+}
+
+
+def cpu_baseline(kind: str, target_s: float):
+    """The oracle, as it stands, on 2^22-parameter slices of the workload: first
+    in this process on one thread for target_s seconds, then in one process
+    per available core (at most 16), each on its own slice, for target_s
+    seconds.  The slices are independent, as the shards are, and every step
+    of the path is element-wise, so the time of a whole step is the
+    parameter count over the measured rate: the extrapolation is stated in
+    the result.  Runs before the GPU is touched."""
     import concurrent.futures as cf
     import multiprocessing as mp
     import platform
 
-    done1, el1 = _cpu_slice_worker(0, target_s)
+    what, psi = CPU_SAMPLES[kind]
+    done1, el1 = _cpu_slice_worker(kind, 0, target_s)
     cores = max(1, min(16, len(os.sched_getaffinity(0))))
     with cf.ProcessPoolExecutor(cores, mp_context=mp.get_context("spawn")) as ex:
         # one warm-up task per worker so that interpreter and import time stay out
-        list(ex.map(_cpu_slice_worker, range(cores), [0.0] * cores))
-        res = list(ex.map(_cpu_slice_worker, range(cores), [target_s] * cores))
+        list(ex.map(_cpu_slice_worker, [kind] * cores, range(cores), [0.0] * cores))
+        res = list(ex.map(_cpu_slice_worker, [kind] * cores, range(cores), [target_s] * cores))
     done_all = sum(r[0] for r in res)
     wall = max(r[1] for r in res)      # the workers' step loops run concurrently
     model = platform.processor() or platform.machine()
@@ -220,14 +313,18 @@ def cpu_baseline(target_s: float):
                 break
     except OSError:
         pass
-    return {"value": done_all / wall, "unit": "params/s", "cores": cores, "kind": "oracle",
-            "sample": (f"oracle sharded step (4 count-weighted BF16 ranks, AdamW, BF16 pack, all-gather) "
-                       f"on 2^22-param slices of the 7B-class layer: {cores} processes, one slice each, "
-                       f"{done_all // CPU_SLICE} slice-steps, the slowest process's loop {wall:.1f} s; numpy ufuncs, one thread "
-                       f"per process; {model}, {os.cpu_count()} CPUs visible, {cores} in the affinity mask "
-                       f"used (capped at 16)"),
-            "single_thread": {"value": done1 / el1, "unit": "params/s", "cores": 1,
-                              "sample": f"{done1 // CPU_SLICE} slice-steps in {el1:.1f} s on one thread"}}
+    rate, rate1 = done_all / wall, done1 / el1
+    return {"value": rate, "unit": "params/s", "cores": cores, "kind": "oracle",
+            "sample": (f"oracle sharded step (reduce-scatter, owner updates with the BF16 pack, all-gather) on "
+                       f"{what}: {cores} processes, one slice each, {done_all // CPU_SLICE} slice-steps, the "
+                       f"slowest process's loop {wall:.1f} s; numpy ufuncs, one thread per process; {model}, "
+                       f"{os.cpu_count()} CPUs visible, {cores} in the affinity mask used (capped at 16). "
+                       f"Extrapolated by parameter count: one {psi:,}-parameter step would take "
+                       f"{psi / rate:.1f} s on {cores} cores and {psi / rate1:.1f} s on one."),
+            "extrapolated_step_s": psi / rate,
+            "single_thread": {"value": rate1, "unit": "params/s", "cores": 1,
+                              "sample": f"{done1 // CPU_SLICE} slice-steps in {el1:.1f} s on one thread",
+                              "extrapolated_step_s": psi / rate1}}
 
 
 # --------------------------------------------------------------------------- flat units
@@ -279,12 +376,20 @@ def run_flat(args, wl, numels, grad_scales=None, counts=None):
         return start.elapsed_time(stop) / args.steps, wall
 
     def sep_step(hp, sample):
+        if not sample:
+            st.reduce_scatter(grads, w)
+            st.update(hp)
+            st.all_gather()
+            return
+        a = T.ev()
         st.reduce_scatter(grads, w)
-        a = T.ev() if sample else None
+        b = T.ev()
         st.update(hp)
-        if sample:
-            T.span(sample, a, T.ev())
+        c = T.ev()
         st.all_gather()
+        T.span("rs", a, b)
+        T.span(sample, b, c)
+        T.span("ag", c, T.ev())
 
     def fused_step(hp, sample):
         a = T.ev() if sample else None
@@ -295,22 +400,11 @@ def run_flat(args, wl, numels, grad_scales=None, counts=None):
 
     ms_step, wall = timed(sep_step, "update4")
     adam_ms = T.ms("update4") / n
-    # breakdown pass for the reduce-scatter and the all-gather (not the timed region)
-    with no_gc():
-        for _ in range(max(4, args.steps // SAMPLE_EVERY)):
-            t += 1
-            a = T.ev()
-            st.reduce_scatter(grads, w)
-            b = T.ev()
-            st.update(wl.hparams(step=t))
-            c = T.ev()
-            st.all_gather()
-            T.span("rs", a, b)
-            T.span("ag", c, T.ev())
-        torch.cuda.synchronize()
+    ev_ms = event_overhead_ms(T, st.all_gather)
+    rs_ms, ag_ms = T.ms("rs") - ev_ms, T.ms("ag") - ev_ms
+    adam_corr = (T.ms("update4") - ev_ms) / n
     pad = st.psi_pad
     step_bytes = (B_RS(n) + B_ADAM + B_AG) * pad
-    rs_ms, ag_ms = T.ms("rs"), T.ms("ag")
     out = _base(wl.description, st.psi / (ms_step * 1e-3), ms_step, args,
                 {"params": st.psi, "n_ranks": n, "storage": "bf16 grads and working weights, fp32 master/m/v",
                  "step": "reduce-scatter + 4 owner Adam updates + all-gather"})
@@ -319,14 +413,19 @@ def run_flat(args, wl, numels, grad_scales=None, counts=None):
         "hbm_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "wall_s_timed": wall,
         "kernels": {
-            "reduce_scatter": {"ms": rs_ms, "bytes": B_RS(n) * pad, "gbs": B_RS(n) * pad / (rs_ms * 1e-3) / 1e9},
-            "adam_shard_step": {"ms": adam_ms, "bytes": B_ADAM * st.shard,
-                                "gbs": B_ADAM * st.shard / (adam_ms * 1e-3) / 1e9,
-                                "timing": f"event pair around the 4 owner updates on every {SAMPLE_EVERY}th "
-                                          "timed step, divided by 4"},
+            "timing": (f"events between the step's kernel groups on every {SAMPLE_EVERY}th step of the timed "
+                       "region, each span less the measured GPU time of one event between two kernels"),
+            "event_overhead_ms": ev_ms,
+            "reduce_scatter": {"ms": rs_ms, "bytes": B_RS(n) * pad, "gbs": B_RS(n) * pad / (rs_ms * 1e-3) / 1e9,
+                               "launches": n},
+            "adam_shard_step": {"ms": adam_corr, "bytes": B_ADAM * st.shard,
+                                "gbs": B_ADAM * st.shard / (adam_corr * 1e-3) / 1e9, "per": "owner launch"},
             "all_gather": {"ms": ag_ms, "bytes": B_AG * pad, "gbs": B_AG * pad / (ag_ms * 1e-3) / 1e9},
+            "sum_ms": rs_ms + n * adam_corr + ag_ms,
         },
-        "roofline": _roofline("adam_shard_step", wl.name, adam_ms, st.shard),
+        "roofline": _roofline("adam_shard_step", wl.name, adam_ms, st.shard,
+                              f"HIP events on the launch stream around the 4 owner updates on every "
+                              f"{SAMPLE_EVERY}th step of the timed region, divided by 4"),
     })
     # the same step with the fused reduce-scatter + update kernel (reduced
     # gradient kept in registers) and the all-gather
@@ -523,7 +622,9 @@ def run_owner_share(args):
         "kernels": {"reduce_scatter": {"ms": rs_ms, "bytes": B_RS(n) * B, "gbs": B_RS(n) * B / (rs_ms * 1e-3) / 1e9},
                     "adam_shard_step": {"ms": adam_ms, "bytes": B_ADAM * B, "gbs": B_ADAM * B / (adam_ms * 1e-3) / 1e9},
                     "timing": f"event pairs around the first bucket on every {SAMPLE_EVERY}th timed step"},
-        "roofline": _roofline("adam_shard_step", wl.name, adam_ms, B),
+        "roofline": _roofline("adam_shard_step", wl.name, adam_ms, B,
+                              f"HIP events on the launch stream around the first bucket's update on every "
+                              f"{SAMPLE_EVERY}th step of the timed region"),
     })
     # the same step with the fused reduce + update kernel per bucket (34 B/param)
     f_ms, _ = timed(fused_step)
@@ -537,7 +638,16 @@ def run_owner_share(args):
 
 
 # --------------------------------------------------------------------------- ZeRO-3 chain
+CHAIN_SAMPLE_UNIT = 17   # layer 16 (unit 0 is the embedding, unit 33 the lm_head)
+
+
 def run_chain(args):
+    """One step: forward, for every unit in order, all-gather of the 4 BF16
+    owner shards into a temporary view that is then released; backward, for
+    every unit in reverse order, reduce-scatter of the 4 ranks' BF16
+    contributions and the 4 owners' Adam updates.  The contributions (the
+    output of a backward computation that is not part of the path) are drawn
+    once, for the largest unit, before the timed region."""
     import torch
 
     import synthetic as S
@@ -559,22 +669,41 @@ def run_chain(args):
     T = Timer()
     U = len(ch.units)
     rg = bool(args.regather_bwd)
-    # The backward computation that produces each unit's N contributions is
-    # not part of the path: they are generated once, for the largest unit,
-    # before the timed region, and every unit's backward reads its prefix.
     fill.chain_unit_grads(gen, wl, 0, ch.grads, ch.max_pad, tmp)
+    del tmp
+    SU = CHAIN_SAMPLE_UNIT
 
-    def step(t, mid=None, fused=False):
+    # sampled steps carry events around the kernel groups of layer 16 and of
+    # the embedding (the lm_head has the embedding's size)
+    SAMPLED = {SU: "layer", 0: "embedding"}
+
+    def step(t, sample=False, mid=None, fused=False):
         hp = wl.hparams(step=t)
         for u in range(U):                      # forward: gather, use, release
-            ch.forward_unit(u)
+            if sample and u in SAMPLED:
+                a = T.ev()
+                ch.forward_unit(u)
+                T.span(SAMPLED[u] + "_ag", a, T.ev())
+            else:
+                ch.forward_unit(u)
         if mid is not None:
             mid.append(T.ev())
         for u in reversed(range(U)):            # backward
             if fused:
                 ch.backward_unit_fused(u, w, hp, regather=rg)
+                continue
+            if rg:
+                ch.forward_unit(u)
+            if sample and u in SAMPLED:
+                a = T.ev()
+                ch.reduce_unit(u, w)
+                b = T.ev()
+                ch.update_unit(u, hp)
+                T.span(SAMPLED[u] + "_rs", a, b)
+                T.span(SAMPLED[u] + "_update4", b, T.ev())
             else:
-                ch.backward_unit(u, w, hp, regather=rg)
+                ch.reduce_unit(u, w)
+                ch.update_unit(u, hp)
 
     t = 0
 
@@ -587,9 +716,9 @@ def run_chain(args):
         with no_gc():
             t0 = time.perf_counter()
             marks = [T.ev()]
-            for _ in range(args.steps):
+            for i in range(args.steps):
                 t += 1
-                step(t, marks, fused=fused)
+                step(t, sample=(i % SAMPLE_EVERY == 0), mid=marks, fused=fused)
                 marks.append(T.ev())
             torch.cuda.synchronize()
             wall = time.perf_counter() - t0
@@ -599,28 +728,37 @@ def run_chain(args):
 
     ms_step, fwd_ms, wall = timed(False)
     bwd_ms = ms_step - fwd_ms
+    adam_ms = T.ms("layer_update4") / n
     f_ms, _, _ = timed(True)
     psi_pad = sum(u[2] for u in ch.units)
     step_bytes = (B_RS(n) + B_ADAM + B_AG * (2 if rg else 1)) * psi_pad
-    # kernel-level timing of one layer unit (not the timed region)
-    lay = 1
-    pad, s = ch.units[lay][2], ch.units[lay][3]
-    hp = wl.hparams(step=t + 1)
-    for _ in range(3):
-        a = T.ev()
-        z.zero_reduce_scatter([g[:pad] for g in ch.grads], w, [g[:s] for g in ch.grad_shards])
-        b = T.ev()
-        T.span("k_rs", a, b)
-        for k in range(n):
-            p, m, v, bb = (x[ch.offsets[lay]:ch.offsets[lay] + s] for x in
-                           (ch.master[k], ch.exp_avg[k], ch.exp_avg_sq[k], ch.bf16[k]))
-            a = T.ev()
-            z.zero_adam_shard_step(p, m, v, bb, ch.grad_shards[k][:s], hp)
-            T.span("k_adam", a, T.ev())
+
+    # per-kernel breakdown from the sampled steps' spans, each less the GPU
+    # time of one event between two kernels (measured here)
+    ev_ms = event_overhead_ms(T, lambda: ch.forward_unit(SU))
+    kern = {"timing": (f"events between the kernel groups of layer 16 and of the embedding on every "
+                       f"{SAMPLE_EVERY}th step of the timed region, each span less the measured GPU time of "
+                       "one event between two kernels; the lm_head is counted with the embedding's figures"),
+            "event_overhead_ms": ev_ms}
+    for name, u, count in (("layer", SU, U - 2), ("embedding", 0, 2)):
+        pad, s = ch.units[u][2], ch.units[u][3]
+        rs = T.ms(name + "_rs") - ev_ms
+        ad = (T.ms(name + "_update4") - ev_ms) / n
+        ag = T.ms(name + "_ag") - ev_ms
+        kern[name] = {
+            "units_per_step": count, "params_padded": pad, "shard": s,
+            "reduce_scatter": {"ms": rs, "bytes": B_RS(n) * pad, "gbs": B_RS(n) * pad / (rs * 1e-3) / 1e9,
+                               "launches": n},
+            "adam_shard_step": {"ms": ad, "bytes": B_ADAM * s, "gbs": B_ADAM * s / (ad * 1e-3) / 1e9,
+                                "per": "owner launch"},
+            "all_gather": {"ms": ag, "bytes": B_AG * pad, "gbs": B_AG * pad / (ag * 1e-3) / 1e9}}
+    kern["sum_ms"] = sum(k["units_per_step"] * (k["reduce_scatter"]["ms"] + n * k["adam_shard_step"]["ms"]
+                                                + k["all_gather"]["ms"] * (2 if rg else 1))
+                         for k in (kern["layer"], kern["embedding"]))
     torch.cuda.synchronize()
     peak = torch.cuda.max_memory_allocated()
-    adam_ms = T.ms("k_adam")
     persistent = sum(x.numel() * x.element_size() for x in ch.master + ch.exp_avg + ch.exp_avg_sq + ch.bf16)
+    s_lay = ch.units[SU][3]
     out = _base(wl.description, wl.psi / (ms_step * 1e-3), ms_step, args,
                 {"params": wl.psi, "n_ranks": n, "units": U, "regather_bwd": rg,
                  "step": "forward: 34 all-gathers into a released view; backward (reverse): "
@@ -630,18 +768,25 @@ def run_chain(args):
     out.update({
         "hbm_gbs_algorithmic": step_bytes / (ms_step * 1e-3) / 1e9,
         "hbm_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "algorithmic_bytes_per_step": step_bytes,
         "forward_ms": fwd_ms, "backward_ms": bwd_ms, "wall_s_timed": wall,
         "memory": {"persistent_bytes_all_owners": persistent,
                    "ledger_zero3_bytes_all_owners": 16 * wl.psi,
                    "peak_allocated_bytes": peak},
-        "kernels": {"reduce_scatter_layer": {"ms": T.ms("k_rs"), "bytes": B_RS(n) * pad},
-                    "adam_shard_step_layer": {"ms": adam_ms, "bytes": B_ADAM * s,
-                                              "gbs": B_ADAM * s / (adam_ms * 1e-3) / 1e9}},
-        "roofline": _roofline("adam_shard_step", wl.name, adam_ms, s),
+        "kernels": kern,
+        "roofline": _roofline("adam_shard_step", wl.name, adam_ms, s_lay,
+                              f"HIP events on the launch stream around the 4 owner updates of layer 16 on every "
+                              f"{SAMPLE_EVERY}th step of the timed region, divided by 4 (the span's one event "
+                              "gap is not subtracted here; kernels.layer has the corrected figure)"),
         "fused_variant": {"ms_per_step": f_ms, "value": wl.psi / (f_ms * 1e-3),
+                          "step": "backward per unit: fused reduce-scatter + owner update (one launch per "
+                                  "owner, the reduced shards kept in registers)",
                           "hbm_gbs_algorithmic": (2 * n + 26 + B_AG * (2 if rg else 1)) * psi_pad
                           / (f_ms * 1e-3) / 1e9},
     })
+    del ch
+    gc.collect()
+    torch.cuda.empty_cache()
     out["copy_ceiling_gbs_same_run"] = copy_ceiling_gbs()
     return out
 
@@ -677,6 +822,89 @@ def _pinned_copy_rates(nbytes):
         torch.cuda.synchronize()
         res["bidir_gbs"] = 2 * nbytes / (time.perf_counter() - t0) / 1e9
     return res
+
+
+def _shard_copy_rates(host, nbytes):
+    """Pinned-copy rates on the offload shard's own pages: host-to-device
+    from the shard's first nbytes, device-to-host into the next nbytes, each
+    alone and both at once on two streams (GB/s).  The shard's contents are
+    overwritten (the step rewrites every chunk at its first micro-batch)."""
+    import torch
+    words = nbytes // 4
+    assert host.numel() >= 2 * words
+    src_h, dst_h = host[:words], host[words:2 * words]
+    d1 = torch.empty(words, dtype=torch.float32, device="cuda")
+    d2 = torch.empty(words, dtype=torch.float32, device="cuda")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    res = {}
+    for _ in range(2):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(s1):
+            d1.copy_(src_h, non_blocking=True)
+        torch.cuda.synchronize()
+        res["h2d_gbs"] = nbytes / (time.perf_counter() - t0) / 1e9
+        t0 = time.perf_counter()
+        with torch.cuda.stream(s2):
+            dst_h.copy_(d2, non_blocking=True)
+        torch.cuda.synchronize()
+        res["d2h_gbs"] = nbytes / (time.perf_counter() - t0) / 1e9
+        t0 = time.perf_counter()
+        with torch.cuda.stream(s1):
+            d1.copy_(src_h, non_blocking=True)
+        with torch.cuda.stream(s2):
+            dst_h.copy_(d2, non_blocking=True)
+        torch.cuda.synchronize()
+        res["bidir_gbs"] = 2 * nbytes / (time.perf_counter() - t0) / 1e9
+    del d1, d2
+    return res
+
+
+def _numa_placement(host):
+    """NUMA nodes of the GPU, of this process's CPUs and of the pinned shard's
+    pages (Linux sysfs, /proc/self/maps and /proc/self/numa_maps); None where
+    the system does not say."""
+    import glob
+
+    import torch
+    out = {"gpu_numa_node": None, "cpu_nodes": None, "shard_pages_by_node": None}
+    try:
+        p = torch.cuda.get_device_properties(0)
+        bdf = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+        out["gpu_pci"] = bdf
+        out["gpu_numa_node"] = int(open(f"/sys/bus/pci/devices/{bdf}/numa_node").read().strip())
+    except Exception as e:          # noqa: BLE001  (diagnostic only)
+        out["gpu_numa_error"] = repr(e)[:120]
+    try:
+        nodes = {}
+        for c in sorted(os.sched_getaffinity(0)):
+            for d in glob.glob(f"/sys/devices/system/cpu/cpu{c}/node*"):
+                k = int(d.rsplit("node", 1)[1])
+                nodes[k] = nodes.get(k, 0) + 1
+        out["cpu_nodes"] = nodes
+    except Exception as e:          # noqa: BLE001
+        out["cpu_nodes_error"] = repr(e)[:120]
+    try:
+        addr = host.data_ptr()
+        start = None
+        for line in open("/proc/self/maps"):
+            lo, hi = (int(x, 16) for x in line.split()[0].split("-"))
+            if lo <= addr < hi:
+                start = lo
+                out["shard_mapping"] = line.strip()[:160]
+                break
+        if start is not None:
+            for line in open("/proc/self/numa_maps"):
+                f = line.split()
+                if int(f[0], 16) == start:
+                    out["shard_numa_maps"] = line.strip()[:200]
+                    pages = {int(x[1:].split("=")[0]): int(x.split("=")[1]) for x in f[2:]
+                             if x.startswith("N") and "=" in x}
+                    out["shard_pages_by_node"] = pages or None
+                    break
+    except Exception as e:          # noqa: BLE001
+        out["shard_pages_error"] = repr(e)[:120]
+    return out
 
 
 def run_offload(args):
@@ -726,12 +954,15 @@ def run_offload(args):
         return 1e3 * _mean(times)
 
     torch.cuda.synchronize()
+    placement = _numa_placement(st.host)
+    shard_before = _shard_copy_rates(st.host, 1 << 30)
     t = 0
     ms_step = timed(False)
     ms_fused = timed(True)
+    shard_after = _shard_copy_rates(st.host, 1 << 30)
     link_bytes = 4 * wl.psi * (M + (M - 1) + 1)     # D2H every mb, H2D from mb 2, H2D stream-back
     link_fused = 4 * wl.psi * ((M - 1) + (M - 1))   # the last micro-batch never crosses the link
-    rates = _pinned_copy_rates(1 << 30)
+    rates = shard_before
     # The schedule's own bound at the measured pinned-copy rates: micro-batch 1
     # only copies to the host, micro-batches 2..M copy both ways (at the
     # bidirectional rate), the stream-back only copies to the device.
@@ -749,7 +980,11 @@ def run_offload(args):
         "bound": "host link (PCIe)",
         "link_gbs": link_bytes / (ms_step * 1e-3) / 1e9,
         "link_bytes_per_step": link_bytes,
-        "pinned_copy_rates_same_process": rates,
+        "pinned_copy_rates_on_shard_before_steps": shard_before,
+        "pinned_copy_rates_on_shard_after_steps": shard_after,
+        "pinned_copy_rates_fresh_buffers_after_steps": _pinned_copy_rates(1 << 30),
+        "schedule_bound_rates": "the shard's own pages, measured before the timed steps",
+        "numa_placement": placement,
         "schedule_bound_ms": sched_ms,
         "frac_of_schedule_bound": sched_ms / ms_step,
         "overlap_efficiency": serial_copy_ms / ms_step,
@@ -769,8 +1004,11 @@ def run_offload(args):
 
 
 def run_copy_calibration(args):
-    """A plain copy kernel of known size for scaling the HBM byte counters:
-    zero_all_gather_layer with one 1 GiB shard (reads 1 GiB, writes 1 GiB)."""
+    """Plain copies of known size for scaling the HBM byte counters, three
+    independent ones: the library's gather kernel with one 1 GiB shard, the
+    runtime's device-to-device copy (torch copy_ of a contiguous tensor, which
+    is hipMemcpyAsync), and a torch element-wise kernel (x * 1 over 2^28
+    float32 values).  Each reads 1 GiB and writes 1 GiB per launch."""
     import torch
 
     import zero_sharded_optimizer_reduce_amd as z
@@ -778,17 +1016,23 @@ def run_copy_calibration(args):
     nbytes = 1 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    srcf, dstf = src.view(torch.float32), dst.view(torch.float32)
     T = Timer()
-    for _ in range(args.warmup):
-        z.zero_all_gather_layer([src], dst)
-    for _ in range(args.steps):
-        a = T.ev()
-        z.zero_all_gather_layer([src], dst)
-        T.span("copy", a, T.ev())
-    torch.cuda.synchronize()
-    ms = T.ms("copy")
-    return {"calibration": "copy", "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
-            "ms": ms, "gbs": 2 * nbytes / (ms * 1e-3) / 1e9, "launches": args.steps + args.warmup}
+    res = {"calibration": "copy", "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
+           "launches_each": args.steps + args.warmup}
+    for name, fn in (("library_gather_kernel", lambda: z.zero_all_gather_layer([src], dst)),
+                     ("runtime_device_to_device_copy", lambda: dst.copy_(src)),
+                     ("torch_elementwise_mul", lambda: torch.mul(srcf, 1.0, out=dstf))):
+        for _ in range(args.warmup):
+            fn()
+        for _ in range(args.steps):
+            a = T.ev()
+            fn()
+            T.span(name, a, T.ev())
+        torch.cuda.synchronize()
+        ms = T.ms(name)
+        res[name] = {"ms": ms, "gbs": 2 * nbytes / (ms * 1e-3) / 1e9}
+    return res
 
 
 RUNNERS = {
@@ -801,14 +1045,24 @@ RUNNERS = {
 }
 
 
+def _nested(result):
+    """A workload's result as an extra key of the line: without the fields the
+    line itself states."""
+    drop = {"metric", "unit", "n_gpus", "steps", "warmup", "higher_is_better", "scaling", "vs_baseline",
+            "dtype", "data"}
+    return {k: v for k, v in result.items() if k not in drop}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="layer7b_weighted_adamw", choices=sorted(RUNNERS))
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="zero3_chain_llama8b", choices=sorted(RUNNERS))
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-layer7b", action="store_true",
+                    help="zero3_chain_llama8b: leave out the 7B-class layer figures that follow the chain")
     ap.add_argument("--regather-bwd", action="store_true",
                     help="zero3_chain_llama8b: gather each unit again before its backward reduce")
     args = ap.parse_args()
@@ -817,8 +1071,8 @@ def main():
               "simulated as buffers in one GPU's HBM and no multi-GPU path is built.", file=sys.stderr)
         sys.exit(2)
     cpu = None
-    if args.workload == "layer7b_weighted_adamw" and not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.cpu_baseline_seconds)    # before anything touches the GPU
+    if args.workload in CPU_SAMPLES and not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload, args.cpu_baseline_seconds)    # before anything touches the GPU
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -828,9 +1082,17 @@ def main():
     if not os.path.exists(_lib.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
+    print(f"bench: {args.workload}, {args.steps} timed steps after {args.warmup} warm-up steps",
+          file=sys.stderr, flush=True)
     out = RUNNERS[args.workload](args)
     if cpu is not None:
         out["cpu_baseline"] = cpu
+    if args.workload == "zero3_chain_llama8b" and not args.no_layer7b:
+        # the chain's buffers are released by now
+        gc.collect()
+        torch.cuda.empty_cache()
+        print("bench: 7B-class layer figures", file=sys.stderr, flush=True)
+        out["layer7b_weighted_adamw"] = _nested(run_layer7b(args))
     print(json.dumps(out), flush=True)
 
 

@@ -70,7 +70,7 @@ TINY = Workload(
 LAYER_7B = Workload(
     name="layer7b_weighted_adamw",
     description=("7B-class layer d=4096 ffn=11008 (202,375,168 params), N=4 ranks "
-                 "weighted by token counts 4096/3072/4096/2048, AdamW wd=0.1, 3 steps"),
+                 "weighted by token counts 4096/3072/4096/2048, AdamW wd=0.1"),
     psi=sum(unit_numels(layer_7b_tensors())), weight_decay=0.1, seed=1,
     extra={"token_counts": [4096, 3072, 4096, 2048], "rank_scale": (0.5, 2.0), "steps": 3})
 

@@ -1,9 +1,12 @@
 """The benchmark's command-line contract on the CPU: more than one GPU is
-refused with a message, and the oracle baseline reports its fields."""
+refused with a message, the default workload is the 8B ZeRO-3 chain, and the
+oracle baseline reports its fields and its extrapolation."""
 import json
 import os
 import subprocess
 import sys
+
+import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -16,15 +19,26 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout.strip() == ""
 
 
-def test_cpu_baseline_fields():
+@pytest.mark.parametrize("kind, psi", [("zero3_chain_llama8b", 8_029_995_008),
+                                       ("layer7b_weighted_adamw", 202_375_168)])
+def test_cpu_baseline_fields(kind, psi):
     sys.path.insert(0, ROOT)
     import bench
-    out = bench.cpu_baseline(0.2)
+    out = bench.cpu_baseline(kind, 0.2)
     json.dumps(out)
     assert out["kind"] == "oracle" and out["unit"] == "params/s"
     assert out["value"] > 0 and out["cores"] >= 1
     assert out["single_thread"]["cores"] == 1 and out["single_thread"]["value"] > 0
-    assert "2^22" in out["sample"]
+    assert "2^22" in out["sample"] and f"{psi:,}" in out["sample"]
+    # the extrapolation to a whole step is the parameter count over the rate
+    assert out["extrapolated_step_s"] == pytest.approx(psi / out["value"])
+
+
+def test_default_workload_is_the_largest_single_gpu_config():
+    import bench
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    assert 'ap.add_argument("--workload", default="zero3_chain_llama8b"' in src
+    assert "zero3_chain_llama8b" in bench.CPU_SAMPLES and "zero3_chain_llama8b" in bench.RUNNERS
 
 
 def test_timed_regions_run_without_the_cyclic_collector():
@@ -50,3 +64,22 @@ def test_timed_regions_run_without_the_cyclic_collector():
         assert not gc.isenabled()      # a caller's own setting is kept
     finally:
         gc.enable()
+
+
+def test_stored_traffic_is_used_only_for_the_device_code_it_measured(tmp_path, monkeypatch, libzero):
+    import bench
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    code = bench.device_code_hash()
+    assert len(code) == 64 and code == bench.device_code_hash()
+    f = tmp_path / "kern_work_traffic.txt"
+    f.write_text(f"# comment: ignored\ndevice_code_sha256: {code}\nparams_per_launch: 100\n"
+                 "hbm_bytes_per_launch: 3000\n")
+    value, source = bench._traffic("kern", "work", 100)
+    assert value == 3000.0 and code[:12] in source and "not from this run" in source
+    assert bench._traffic("kern", "work", 99)[0] is None                 # another launch size
+    assert bench._traffic("other", "work", 100)[0] is None               # no summary
+    f.write_text(f"device_code_sha256: {'0' * 64}\nparams_per_launch: 100\nhbm_bytes_per_launch: 3000\n")
+    value, source = bench._traffic("kern", "work", 100)
+    assert value is None and "other device code" in source
+    with pytest.raises(ValueError):
+        bench._elf_section(__file__, ".hip_fatbin")                      # not an ELF file

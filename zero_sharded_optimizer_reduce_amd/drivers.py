@@ -225,11 +225,21 @@ class Zero3Chain:
         weights are first gathered again into the view, as the backward pass
         needs them (essay, ZeRO-3 的一次完整计算: backward gathers each layer
         again before computing its gradient)."""
-        pad, s = self.units[u][2], self.units[u][3]
         if regather:
             self.forward_unit(u, stream=stream)
+        self.reduce_unit(u, weights, stream=stream)
+        self.update_unit(u, hp, stream=stream)
+
+    def reduce_unit(self, u: int, weights, stream=None):
+        """Unit u's N contributions reduce-scattered into the owners' FP32
+        gradient shards."""
+        pad, s = self.units[u][2], self.units[u][3]
         zero_reduce_scatter([g[:pad] for g in self.grads], weights,
                             [g[:s] for g in self.grad_shards], stream=stream)
+
+    def update_unit(self, u: int, hp, stream=None):
+        """Each owner's update of its slice of unit u from its gradient shard."""
+        s = self.units[u][3]
         for k, (p, m, v, b) in enumerate(zip(*(self.owner_slices(u, x) for x in
                                               (self.master, self.exp_avg, self.exp_avg_sq, self.bf16)))):
             zero_adam_shard_step(p, m, v, b, self.grad_shards[k][:s], hp, stream=stream)
