@@ -49,6 +49,8 @@ extern "C" {
 #define ZERO_MAX_RANKS 16   /* upper bound on n_ranks and n_shards */
 #define ZERO_NORM_BLOCKS 1024  /* partial sums per shard in zero_grad_norm_sq */
 #define ZERO_OFFLOAD_MAX_CHUNKS 65536  /* upper bound on ceil(shard/chunk) of an offload handle */
+/* doubles in the library's own partial-sum array of zero_grad_norm_sq_no_alloc (128 KiB per GPU) */
+#define ZERO_NORM_SCRATCH_DOUBLES (ZERO_MAX_RANKS * ZERO_NORM_BLOCKS)
 
 typedef enum zero_status {
   ZERO_OK = 0,
@@ -182,6 +184,28 @@ int zero_adam_shard_step_scaled(float* master, float* exp_avg, float* exp_avg_sq
 int zero_grad_norm_sq(const float* const* shards, int n_shards, int64_t shard_numel,
                       double* workspace, int64_t workspace_len, double* norm_sq_out,
                       float max_norm, float* clip_coef_out, void* stream);
+
+/* zero_grad_norm_sq without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The per-block partial sums go to an array
+ * of ZERO_NORM_SCRATCH_DOUBLES doubles (128 KiB) that the library itself
+ * holds in every GPU it runs on, until the process ends; its address on a
+ * device is looked up on the first call with that device current.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ * Same kernels, summation order and bits as zero_grad_norm_sq.
+ *   shards, n_shards, shard_numel, norm_sq_out, max_norm, clip_coef_out,
+ *   stream: as zero_grad_norm_sq.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on one GPU (other streams, other threads) race on it and give wrong
+ * results, so the caller serialises them.  Nothing carries over between
+ * calls: each call's first pass writes every partial sum its second pass
+ * reads, so the array needs no clearing.
+ * Errors: as zero_grad_norm_sq; ZERO_ERR_SIZE if n_shards*ZERO_NORM_BLOCKS
+ * partial sums would not fit the array (not reachable with n_shards <= 16);
+ * ZERO_ERR_HIP if the array's device address cannot be obtained. */
+int zero_grad_norm_sq_no_alloc(const float* const* shards, int n_shards, int64_t shard_numel,
+                               double* norm_sq_out, float max_norm, float* clip_coef_out,
+                               void* stream);
 
 /* Reduce-scatter and owner update in one pass ([blog] 三级分片, ZeRO-1: the
  * optimizer step sits between the reduce-scatter and the all-gather).  For

@@ -17,6 +17,7 @@ from .api import (  # noqa: F401
     zero_adam_shard_step_scaled,
     zero_all_gather_layer,
     zero_grad_norm_sq,
+    zero_grad_norm_sq_no_alloc,
     zero_last_path_vectorized,
     zero_offload_create,
     zero_offload_destroy,

@@ -44,6 +44,7 @@ SIGNATURES = {
     "zero_adam_shard_step": (C.c_int, [P, P, P, P, P, I64, C.POINTER(AdamHparams), P]),
     "zero_adam_shard_step_scaled": (C.c_int, [P, P, P, P, P, P, I64, C.POINTER(AdamHparams), P]),
     "zero_grad_norm_sq": (C.c_int, [PP, C.c_int, I64, P, I64, P, C.c_float, P, P]),
+    "zero_grad_norm_sq_no_alloc": (C.c_int, [PP, C.c_int, I64, P, C.c_float, P, P]),
     "zero_reduce_scatter_adam": (C.c_int, [PP, FP, C.c_int, I64, C.c_int, PP, PP, PP, PP, PP, PP,
                                            C.POINTER(AdamHparams), P]),
     "zero_adam_shard_step_dev": (C.c_int, [P, P, P, P, P, P, I64, P, P]),

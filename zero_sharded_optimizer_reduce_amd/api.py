@@ -140,29 +140,44 @@ def zero_adam_shard_step_scaled(master, exp_avg, exp_avg_sq, bf16_out, grad, gra
           "zero_adam_shard_step_scaled")
 
 
+def _norm_args(name, shards, norm_sq_out, clip_coef_out):
+    n = len(shards)
+    if n < 1:
+        raise ValueError(f"{name}: no shards")
+    numel = shards[0].numel()
+    sp = [_dev(t, f"shards[{k}]", (torch.float32,)) for k, t in enumerate(shards)]
+    if any(t.numel() != numel for t in shards):
+        raise ValueError(f"{name}: shards differ in size")
+    op = _dev(norm_sq_out, "norm_sq_out", (torch.float64,))
+    if norm_sq_out.numel() < 1:
+        raise ValueError(f"{name}: norm_sq_out needs one element")
+    cp = None
+    if clip_coef_out is not None:
+        cp = _dev(clip_coef_out, "clip_coef_out", (torch.float32,))
+        if clip_coef_out.numel() < 1:
+            raise ValueError(f"{name}: clip_coef_out needs one element")
+    return _ptrs(sp), n, numel, op, cp
+
+
 def zero_grad_norm_sq(shards: Sequence[torch.Tensor], workspace: torch.Tensor, norm_sq_out: torch.Tensor,
                       max_norm: float = 0.0, clip_coef_out: Optional[torch.Tensor] = None, stream=None) -> None:
     """norm_sq_out[0] (FP64 device tensor) = sum of squares of all shards
     (deterministic order); clip_coef_out[0] (FP32) = min(1, max_norm/(norm+1e-6))
     when given.  workspace: FP64 device tensor of >= len(shards)*1024 elements."""
-    n = len(shards)
-    if n < 1:
-        raise ValueError("zero_grad_norm_sq: no shards")
-    numel = shards[0].numel()
-    sp = [_dev(t, f"shards[{k}]", (torch.float32,)) for k, t in enumerate(shards)]
-    if any(t.numel() != numel for t in shards):
-        raise ValueError("zero_grad_norm_sq: shards differ in size")
+    sp, n, numel, op, cp = _norm_args("zero_grad_norm_sq", shards, norm_sq_out, clip_coef_out)
     wp = _dev(workspace, "workspace", (torch.float64,))
-    op = _dev(norm_sq_out, "norm_sq_out", (torch.float64,))
-    if norm_sq_out.numel() < 1:
-        raise ValueError("zero_grad_norm_sq: norm_sq_out needs one element")
-    cp = None
-    if clip_coef_out is not None:
-        cp = _dev(clip_coef_out, "clip_coef_out", (torch.float32,))
-        if clip_coef_out.numel() < 1:
-            raise ValueError("zero_grad_norm_sq: clip_coef_out needs one element")
-    check(load().zero_grad_norm_sq(_ptrs(sp), n, numel, wp, workspace.numel(), op, float(max_norm), cp,
+    check(load().zero_grad_norm_sq(sp, n, numel, wp, workspace.numel(), op, float(max_norm), cp,
                                    _stream(stream)), "zero_grad_norm_sq")
+
+
+def zero_grad_norm_sq_no_alloc(shards: Sequence[torch.Tensor], norm_sq_out: torch.Tensor, max_norm: float = 0.0,
+                               clip_coef_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """zero_grad_norm_sq with the partial sums in the library's own per-GPU
+    array instead of a caller workspace: nothing is allocated.  Calls that
+    overlap in time on one GPU race on that array."""
+    sp, n, numel, op, cp = _norm_args("zero_grad_norm_sq_no_alloc", shards, norm_sq_out, clip_coef_out)
+    check(load().zero_grad_norm_sq_no_alloc(sp, n, numel, op, float(max_norm), cp, _stream(stream)),
+          "zero_grad_norm_sq_no_alloc")
 
 
 def _fused_args(name, rank_grads, rank_weights, master, exp_avg, exp_avg_sq, bf16_out, grad_out, grad_acc):

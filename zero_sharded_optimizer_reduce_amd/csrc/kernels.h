@@ -34,6 +34,11 @@ struct AdamParams {
 // summation order never depends on the device.
 constexpr int kNormBlocks = ZERO_NORM_BLOCKS;
 
+// Doubles of the library-owned partial-sum array of zero_grad_norm_sq_no_alloc
+// (one array per GPU): room for every shard's partial sums.
+constexpr int kNormScratchDoubles = ZERO_NORM_SCRATCH_DOUBLES;
+static_assert(kNormScratchDoubles >= ZERO_MAX_RANKS * kNormBlocks, "scratch holds every partial sum");
+
 struct NormParams {
   const float* x[ZERO_MAX_RANKS];  // shards
   int64_t n;                       // elements per shard
@@ -84,6 +89,11 @@ hipError_t launch_gather(const GatherParams& p, int n_shards, int path, hipStrea
 // Two passes: per-(block, shard) partial sums of squares, then one block
 // folds them in index order and derives the clip coefficient.
 hipError_t launch_norm(NormParams& p, bool vec, hipStream_t stream);
+
+// Device address of the current device's partial-sum array for the norm
+// (kNormScratchDoubles doubles, 256-byte aligned).  Looked up once per device
+// with that device current and cached; allocates nothing.
+hipError_t norm_scratch_device_ptr(double** out);
 
 // zero_adam_scalars_fetch: ring is the device-visible address of the pinned
 // host ring, ring_len a power of two.

@@ -18,6 +18,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -373,6 +374,12 @@ __global__ __launch_bounds__(kBlock) void norm_partial_kernel(NormParams p) {
   const double t = block_sum(acc);
   if (threadIdx.x == 0) p.partials[static_cast<int64_t>(k) * gridDim.x + blockIdx.x] = t;
 }
+
+// Partial sums of zero_grad_norm_sq_no_alloc: one array per GPU, held until the
+// process ends.  Host code never uses this name as an address: it is a
+// host-side stand-in for the symbol, and the device address comes from
+// norm_scratch_device_ptr.
+static __device__ __align__(256) double norm_scratch[kNormScratchDoubles];
 
 __global__ __launch_bounds__(kBlock) void norm_final_kernel(NormParams p) {
   const int64_t total = static_cast<int64_t>(p.n_shards) * p.gx;
@@ -776,6 +783,32 @@ hipError_t launch_norm(NormParams& p, bool vec, hipStream_t s) {
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(norm_final_kernel, dim3(1), dim3(kBlock), 0, s, p);
   return hipGetLastError();
+}
+
+hipError_t norm_scratch_device_ptr(double** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<double*> cache[kMaxDevices];
+  static std::mutex lookup;
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  double* p = cache[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> g(lookup);
+    p = cache[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* addr = nullptr;
+      // with `dev` current: this device's copy of the array
+      err = hipGetSymbolAddress(&addr, HIP_SYMBOL(norm_scratch));
+      if (err != hipSuccess) return err;
+      if (!addr) return hipErrorInvalidSymbol;
+      p = static_cast<double*>(addr);
+      cache[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 hipError_t launch_gather(const GatherParams& p, int n_shards, int path, hipStream_t s) {

@@ -234,6 +234,37 @@ int zero_grad_norm_sq(const float* const* shards, int n_shards, int64_t shard_nu
   return hip_status(launch_norm(p, vec, static_cast<hipStream_t>(stream)), "zero_grad_norm_sq");
 }
 
+int zero_grad_norm_sq_no_alloc(const float* const* shards, int n_shards, int64_t shard_numel,
+                               double* norm_sq_out, float max_norm, float* clip_coef_out,
+                               void* stream) {
+  TraceRange tr("zero_grad_norm_sq_no_alloc");
+  double* scratch_dev = nullptr;
+  int st = hip_status(norm_scratch_device_ptr(&scratch_dev), "zero_grad_norm_sq_no_alloc: scratch address");
+  if (st) return st;
+  if (n_shards >= 1 && n_shards <= ZERO_MAX_RANKS &&
+      static_cast<int64_t>(n_shards) * ZERO_NORM_BLOCKS > kNormScratchDoubles)
+    return fail(ZERO_ERR_SIZE, "grad_norm_no_alloc: the partial sums exceed the library's array");
+  Err e;
+  st = check_grad_norm(shards, n_shards, shard_numel, scratch_dev, kNormScratchDoubles, norm_sq_out,
+                       max_norm, clip_coef_out, e);
+  if (st) return fail(st, e.msg);
+  NormParams p;
+  memset(&p, 0, sizeof p);
+  p.n = shard_numel;
+  p.n_shards = n_shards;
+  p.partials = scratch_dev;
+  p.out = norm_sq_out;
+  p.coef = clip_coef_out;
+  p.max_norm = max_norm;
+  bool vec = true;
+  for (int k = 0; k < n_shards; ++k) {
+    p.x[k] = shards[k];
+    vec = vec && aligned16(shards[k]);
+  }
+  set_path(vec);
+  return hip_status(launch_norm(p, vec, static_cast<hipStream_t>(stream)), "zero_grad_norm_sq_no_alloc");
+}
+
 int zero_adam_shard_step_dev(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* bf16_out,
                              const float* grad, const float* grad_scale, int64_t n,
                              const zero_adam_scalars* scalars_dev, void* stream) {
