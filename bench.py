@@ -11,9 +11,10 @@ shards are all-gathered into a temporary view, which is released.  Backward,
 units in reverse order: reduce-scatter of the 4 ranks' BF16 contributions
 into 4 FP32 owner shards, then the 4 owners' fused Adam updates (FP32 master,
 m, v and the BF16 working shard).  Inputs are resident in HBM before the timed
-region.  After the chain's buffers are released the same line carries the
-7B-class layer figures (d=4096, ffn=11008, 202,375,168 parameters, ranks
-weighted by token counts, AdamW wd=0.1) under an extra key.
+region.  The same line carries the 7B-class layer figures (d=4096,
+ffn=11008, 202,375,168 parameters, ranks weighted by token counts, AdamW
+wd=0.1) under an extra key, measured in a child process that runs before this
+process touches the GPU.
 
 Other workloads (--workload): tiny_flat_1m, layer7b_weighted_adamw,
 owner_share_8b_buckets (one owner's 2.0e9-parameter share in 64M buckets),
@@ -1053,6 +1054,23 @@ def _nested(result):
     return {k: v for k, v in result.items() if k not in drop}
 
 
+def _child_workload(name, args):
+    """Run one workload of this script in a child process and return its line
+    (as an extra key).  Started before this process touches the GPU, so the
+    two never use it at once and the child's buffers are its own fresh
+    allocations; the child's progress lines go to stderr as they come."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--workload", name, "--no-cpu-baseline",
+           "--steps", str(args.steps), "--warmup", str(args.warmup)]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=900)
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    if r.returncode != 0 or not lines:
+        return {"error": f"{' '.join(cmd[1:])} exited with {r.returncode}"}
+    out = _nested(json.loads(lines[-1]))
+    out["process"] = "a child process of this run, before this process used the GPU"
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -1073,6 +1091,10 @@ def main():
     cpu = None
     if args.workload in CPU_SAMPLES and not args.no_cpu_baseline:
         cpu = cpu_baseline(args.workload, args.cpu_baseline_seconds)    # before anything touches the GPU
+    layer = None
+    if args.workload == "zero3_chain_llama8b" and not args.no_layer7b:
+        print("bench: 7B-class layer figures (child process)", file=sys.stderr, flush=True)
+        layer = _child_workload("layer7b_weighted_adamw", args)
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -1087,12 +1109,8 @@ def main():
     out = RUNNERS[args.workload](args)
     if cpu is not None:
         out["cpu_baseline"] = cpu
-    if args.workload == "zero3_chain_llama8b" and not args.no_layer7b:
-        # the chain's buffers are released by now
-        gc.collect()
-        torch.cuda.empty_cache()
-        print("bench: 7B-class layer figures", file=sys.stderr, flush=True)
-        out["layer7b_weighted_adamw"] = _nested(run_layer7b(args))
+    if layer is not None:
+        out["layer7b_weighted_adamw"] = layer
     print(json.dumps(out), flush=True)
 
 

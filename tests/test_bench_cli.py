@@ -83,3 +83,12 @@ def test_stored_traffic_is_used_only_for_the_device_code_it_measured(tmp_path, m
     assert value is None and "other device code" in source
     with pytest.raises(ValueError):
         bench._elf_section(__file__, ".hip_fatbin")                      # not an ELF file
+
+
+def test_child_workload_failure_is_reported_not_raised():
+    # without a GPU the child exits with an error; the line records it
+    import argparse
+
+    import bench
+    out = bench._child_workload("layer7b_weighted_adamw", argparse.Namespace(steps=1, warmup=0))
+    assert "error" in out and "exited with 1" in out["error"]
