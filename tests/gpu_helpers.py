@@ -2,6 +2,9 @@
 patterns and FP32 arrays, and the parity bar."""
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -54,3 +57,19 @@ def assert_state_close(p, m, v, b, ref, what=""):
     assert max(u) <= FP32_ULP_TOL and ub <= BF16_ULP_TOL, \
         f"{what}: ulps master/m/v {u}, bf16 {ub} (asserted 0; graded bar {FP32_ULP_BAR}/{BF16_ULP_BAR})"
     return u, ub
+
+
+CHUNK = 1 << 22     # elements per work item of the full-array comparisons
+
+
+def chunked(n: int, fn, chunk: int = CHUNK):
+    """fn(lo, hi) over [0, n) in independent chunk-sized pieces on a thread
+    pool (numpy releases the GIL inside its array loops); results in order."""
+    workers = min(16, max(1, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(lambda lo: fn(lo, min(n, lo + chunk)), range(0, n, chunk)))
+
+
+def max_ulps(results):
+    """Combine assert_state_close results ((u_p, u_m, u_v), u_b) of many chunks."""
+    return tuple(max(r[0][i] for r in results) for i in range(3)), max(r[1] for r in results)

@@ -12,15 +12,14 @@
 * The same layer with the global gradient-norm clip, at full size: the FP64
   norm against the oracle's, the clip coefficient, and the scaled update.
 """
-import os
-
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import synthetic as S
-from gpu_helpers import (assert_grad_exact, assert_state_close, bf16_to_dev, bf16_to_host, f32_to_host)
+from gpu_helpers import (assert_grad_exact, assert_state_close, bf16_to_dev, bf16_to_host, chunked,
+                         f32_to_host, max_ulps)
 
 pytestmark = pytest.mark.gpu
 
@@ -68,22 +67,16 @@ def _windows(psi_pad, n, shard, rng, width=4096, n_random=6):
     return sorted(starts)
 
 
-CHUNK = 1 << 22     # elements per oracle work item of the full-array comparison
-
-
 def _full_step_check(host_g, w, cpu_state, gpu_grad, gpu_state, sc, what):
     """The oracle's reduction and AdamW step over every element, in independent
-    2^22-element chunks on a thread pool (numpy releases the GIL in its array
-    loops), each compared with the GPU's arrays: the reduced gradient bit for
-    bit, master/m/v/BF16 at ulp distance 0.  cpu_state (p, m, v) is advanced
-    in place to the oracle's new state.  Returns the max ulps seen."""
-    from concurrent.futures import ThreadPoolExecutor
-    psi = host_g[0].size
+    chunks on a thread pool, each compared with the GPU's arrays: the reduced
+    gradient bit for bit, master/m/v/BF16 at ulp distance 0.  cpu_state
+    (p, m, v) is advanced in place to the oracle's new state.  Returns the
+    max ulps seen."""
     cp, cm, cv = cpu_state
     gp, gm, gv, gb = gpu_state
 
-    def work(lo):
-        hi = min(psi, lo + CHUNK)
+    def work(lo, hi):
         g_ref = oracle.reduce_full([h[lo:hi] for h in host_g], w)
         assert_grad_exact(gpu_grad[lo:hi], g_ref, f"{what}, reduced gradient [{lo}, {hi})")
         ref = oracle.adam_step(cp[lo:hi], cm[lo:hi], cv[lo:hi], g_ref, sc)
@@ -91,9 +84,7 @@ def _full_step_check(host_g, w, cpu_state, gpu_grad, gpu_state, sc, what):
         cp[lo:hi], cm[lo:hi], cv[lo:hi] = ref[0], ref[1], ref[2]
         return u
 
-    with ThreadPoolExecutor(min(16, max(1, len(os.sched_getaffinity(0))))) as ex:
-        res = list(ex.map(work, range(0, psi, CHUNK)))
-    return tuple(max(r[0][i] for r in res) for i in range(3)), max(r[1] for r in res)
+    return max_ulps(chunked(host_g[0].size, work))
 
 
 def test_layer7b_three_adamw_steps():

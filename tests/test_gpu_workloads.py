@@ -1,16 +1,19 @@
 """GPU parity at full size, in the launch configuration bench.py times, on
-sampled outputs the oracle computes on the host:
+whole sampled units that the oracle recomputes on the host, every element
+compared (the reduced gradients bit for bit, the state at ulp distance 0):
 
 * one owner's 2.0e9-parameter share updated in 30 buckets of 2^26 (t=1000,
-  wd=0.1): the first bucket, the partial last bucket and random windows;
-* the ZeRO-3 chain over the 8B Llama-like model's 34 units: gathered views of
-  sampled units, and reduced gradients and updated state of sampled units
-  (embedding, first/middle/last layer, lm_head);
+  wd=0.1): the first bucket, the partial last bucket and 3 seeded random
+  buckets;
+* the ZeRO-3 chain over the 8B Llama-like model's 34 units: the embedding,
+  the lm_head and 3 seeded random layers: their gathered views, reduced
+  gradients and updated state;
 * the host-offloaded 2.0e9-parameter gradient shard through two slots over 4
-  micro-batches: windows of the first, the partial last and random chunks.
+  micro-batches: the first chunk, the partial last chunk and 3 seeded random
+  chunks, both the host accumulation and the updated state.
 
 Inputs are drawn on the device with keyed generators (synthetic.fill) and the
-checked regions are copied to the host (or regenerated from their keys)."""
+checked units are copied to the host (or regenerated from their keys)."""
 import gc
 
 import numpy as np
@@ -19,7 +22,8 @@ import torch
 
 import oracle
 import synthetic as S
-from gpu_helpers import assert_grad_exact, assert_state_close, bf16_to_host, f32_to_host
+from gpu_helpers import (assert_grad_exact, assert_state_close, bf16_to_host, chunked, f32_to_host,
+                         max_ulps)
 from synthetic import fill
 from synthetic.workloads import BUCKET, CHAIN_8B, OFFLOAD_8B, OWNER_8B
 
@@ -28,11 +32,14 @@ pytestmark = pytest.mark.gpu
 import zero_sharded_optimizer_reduce_amd as z  # noqa: E402  (a broken package must fail, not skip)
 from zero_sharded_optimizer_reduce_amd.drivers import BucketedOwnerStep, OffloadStep, Zero3Chain  # noqa: E402
 
-W = 1 << 16     # window width
-
 
 def _sc(hp):
     return oracle.adam_scalars(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"], hp["step"])
+
+
+def _first_last_random(n, rng, k=3):
+    """Indices 0 and n-1 and k seeded random ones between them."""
+    return [0, n - 1] + sorted(int(x) for x in rng.choice(np.arange(1, n - 1), k, replace=False))
 
 
 @pytest.fixture(autouse=True)
@@ -53,54 +60,39 @@ def test_owner_share_buckets_full_size():
     del tmp
     nb = len(st.bounds)
     assert nb == 30 and st.bounds[-1][1] - st.bounds[-1][0] == wl.psi - 29 * BUCKET
-    rng = np.random.default_rng(wl.seed)
-    regions = [st.bounds[0], st.bounds[-1]]                      # whole first and last buckets
-    for b in rng.choice(np.arange(1, nb - 1), 3, replace=False):
-        lo = st.bounds[b][0] + int(rng.integers(0, BUCKET - W))
-        regions.append((lo, lo + W))
+    picks = _first_last_random(nb, np.random.default_rng(wl.seed))
     w = z.zero_rank_weights(None, n)
     hp = wl.hparams(step=wl.step0)
-    pre = []
-    for lo, hi in regions:
-        print(f"owner share: region [{lo}, {hi})", flush=True)
-        g = [bf16_to_host(c[lo:hi]) for c in st.contrib]
-        pre.append((g, f32_to_host(st.master[lo:hi]), f32_to_host(st.exp_avg[lo:hi]),
-                    f32_to_host(st.exp_avg_sq[lo:hi])))
-        # the reduced gradient of the region, bit-exact (reduce is pure)
+    pre = {}
+    for b in picks:
+        lo, hi = st.bounds[b]
+        print(f"owner share: bucket {b} [{lo}, {hi})", flush=True)
+        # the reduced gradient of the bucket, as the step computes it (the
+        # step's own bucket buffer is reused, so it is taken here)
         red = torch.empty(hi - lo, dtype=torch.float32, device="cuda")
         z.zero_reduce_scatter([c[lo:hi] for c in st.contrib], w, [red])
-        assert_grad_exact(f32_to_host(red), oracle.reduce_full(g, w), f"region {lo}")
-    # the inputs were drawn from keys: regenerating one region gives the same values
-    lo, hi = regions[2]
-    assert np.array_equal(f32_to_host(fill.owner_share_region(gen, wl, "v", lo, hi)), pre[2][3])
+        pre[b] = ([bf16_to_host(c[lo:hi]) for c in st.contrib], f32_to_host(st.master[lo:hi]),
+                  f32_to_host(st.exp_avg[lo:hi]), f32_to_host(st.exp_avg_sq[lo:hi]), f32_to_host(red))
+        del red
+    # the inputs were drawn from keys: regenerating one bucket gives the same values
+    lo, hi = st.bounds[picks[2]]
+    assert np.array_equal(f32_to_host(fill.owner_share_region(gen, wl, "v", lo, hi)), pre[picks[2]][3])
     st.step(w, hp)
     torch.cuda.synchronize()
     sc = _sc(hp)
-    for (lo, hi), (g, p, m, v) in zip(regions, pre):
-        ref = oracle.adam_step(p, m, v, oracle.reduce_full(g, w), sc)
-        assert_state_close(f32_to_host(st.master[lo:hi]), f32_to_host(st.exp_avg[lo:hi]),
-                           f32_to_host(st.exp_avg_sq[lo:hi]), bf16_to_host(st.bf16[lo:hi]), ref,
-                           f"region [{lo}, {hi})")
+    for b in picks:
+        lo, hi = st.bounds[b]
+        g, p, m, v, gpu_red = pre[b]
+        got = (f32_to_host(st.master[lo:hi]), f32_to_host(st.exp_avg[lo:hi]), f32_to_host(st.exp_avg_sq[lo:hi]),
+               bf16_to_host(st.bf16[lo:hi]))
 
+        def work(a, e):
+            red = oracle.reduce_full([x[a:e] for x in g], w)
+            assert_grad_exact(gpu_red[a:e], red, f"bucket {b} [{a}, {e})")
+            ref = oracle.adam_step(p[a:e], m[a:e], v[a:e], red, sc)
+            return assert_state_close(*(x[a:e] for x in got), ref, f"bucket {b} [{a}, {e})")
 
-def _unit_windows(pad, s, n, rng):
-    starts = {0, pad - W}
-    for k in range(1, n):
-        starts.add(k * s - W // 2)                 # straddles an owner boundary
-    starts.update(int(x) for x in rng.integers(0, pad - W, 2))
-    return sorted(starts)
-
-
-def _owner_pieces(a, s):
-    """Split the unit window [a, a+W) into (owner k, [j0, j1) in k's shard,
-    offset of the piece inside the window)."""
-    out, pos = [], a
-    while pos < a + W:
-        k, j0 = pos // s, pos % s
-        j1 = min(s, j0 + (a + W - pos))
-        out.append((k, j0, j1, pos - a))
-        pos += j1 - j0
-    return out
+        print(f"owner share: bucket {b}: {hi - lo} elements, max ulp {max_ulps(chunked(hi - lo, work))}", flush=True)
 
 
 def test_zero3_chain_full_size():
@@ -114,15 +106,14 @@ def test_zero3_chain_full_size():
         for lo, hi in fill.pieces(ch.owner_numel):
             ch.bf16[k][lo:hi].copy_(ch.master[k][lo:hi])
     U = len(ch.units)
-    sampled = [0, 1, 16, U - 2, U - 1]
-    rng = np.random.default_rng(wl.seed)
-    wins, pre = {}, {}
-    for u in sampled:
-        _, psi, pad, s = ch.units[u]
-        off = ch.offsets[u]
-        wins[u] = _unit_windows(pad, s, n, rng)
-        pre[u] = [np.concatenate([f32_to_host(ch.master[k][off + j0: off + j1])
-                                  for k, j0, j1, _ in _owner_pieces(a, s)]) for a in wins[u]]
+    sampled = _first_last_random(U, np.random.default_rng(wl.seed))
+
+    def flat(bufs, u, host=f32_to_host):
+        """Unit u of per-owner buffers as one flat array in owner order."""
+        s, off = ch.units[u][3], ch.offsets[u]
+        return np.concatenate([host(b[off:off + s]) for b in bufs])
+
+    pre = {u: flat(ch.master, u) for u in sampled}        # m = v = 0 before the first step
     w = z.zero_rank_weights(None, n)
     hp = wl.hparams(step=1)
     tmp = torch.empty(ch.max_pad, dtype=torch.float32, device="cuda")
@@ -130,37 +121,34 @@ def test_zero3_chain_full_size():
     for u in range(U):
         view = ch.forward_unit(u)
         if u in sampled:
-            _, psi, pad, s = ch.units[u]
-            off = ch.offsets[u]
             torch.cuda.synchronize()
-            for a in wins[u]:
-                exp = oracle.all_gather([bf16_to_host(ch.bf16[k][off + j0: off + j1])
-                                         for k, j0, j1, _ in _owner_pieces(a, s)])
-                assert np.array_equal(bf16_to_host(view[a:a + W]), exp), (u, a)
+            print(f"chain: view of unit {u} ({ch.units[u][0]}, {ch.units[u][2]} elements)", flush=True)
+            assert np.array_equal(bf16_to_host(view), oracle.all_gather(
+                [bf16_to_host(ch.bf16[k][ch.offsets[u]:ch.offsets[u] + ch.units[u][3]]) for k in range(n)])), u
     # backward in reverse order
     sc = _sc(hp)
     for u in reversed(range(U)):
-        pad = ch.units[u][2]
+        pad, s = ch.units[u][2], ch.units[u][3]
         fill.chain_unit_grads(gen, wl, u, ch.grads, pad, tmp)
         ch.backward_unit(u, w, hp)
         if u not in sampled:
             continue
-        print(f"chain: checking unit {u}", flush=True)
         torch.cuda.synchronize()
-        _, psi, pad, s = ch.units[u]
-        off = ch.offsets[u]
-        for a, p0 in zip(wins[u], pre[u]):
-            g = [bf16_to_host(x[a:a + W]) for x in ch.grads]
-            red = oracle.reduce_full(g, w)
-            z0 = np.zeros(W, np.float32)
-            ref = oracle.adam_step(p0, z0, z0.copy(), red, sc)
-            parts = _owner_pieces(a, s)
-            gpu_red = np.concatenate([f32_to_host(ch.grad_shards[k][j0:j1]) for k, j0, j1, _ in parts])
-            assert_grad_exact(gpu_red, red, f"unit {u} window {a}")
-            got = [np.concatenate([f32_to_host(x[k][off + j0: off + j1]) for k, j0, j1, _ in parts])
-                   for x in (ch.master, ch.exp_avg, ch.exp_avg_sq)]
-            got_b = np.concatenate([bf16_to_host(ch.bf16[k][off + j0: off + j1]) for k, j0, j1, _ in parts])
-            assert_state_close(*got, got_b, ref, f"unit {u} window {a}")
+        g = [bf16_to_host(x[:pad]) for x in ch.grads]
+        gpu_red = np.concatenate([f32_to_host(x[:s]) for x in ch.grad_shards])
+        got = (flat(ch.master, u), flat(ch.exp_avg, u), flat(ch.exp_avg_sq, u), flat(ch.bf16, u, bf16_to_host))
+        p0 = pre.pop(u)
+
+        def work(a, e):
+            red = oracle.reduce_full([x[a:e] for x in g], w)
+            assert_grad_exact(gpu_red[a:e], red, f"unit {u} [{a}, {e})")
+            z0 = np.zeros(e - a, np.float32)
+            ref = oracle.adam_step(p0[a:e], z0, z0.copy(), red, sc)
+            return assert_state_close(*(x[a:e] for x in got), ref, f"unit {u} [{a}, {e})")
+
+        print(f"chain: unit {u} ({ch.units[u][0]}): {pad} elements, max ulp {max_ulps(chunked(pad, work))}",
+              flush=True)
+        del g, gpu_red, got, p0
 
 
 @pytest.mark.parametrize("fuse_last", [False, True])
@@ -172,15 +160,9 @@ def test_offload_full_size(fuse_last):
     tmp = torch.empty(C, dtype=torch.float32, device="cuda")
     fill.fill_normal_pieces(gen, st.master, wl.master_sigma, fill.K_MASTER)
     nc = st.n_chunks
-    assert nc == 30
-    rng = np.random.default_rng(wl.seed)
-    chunks = [0, nc - 1] + [int(c) for c in rng.choice(np.arange(1, nc - 1), 3, replace=False)]
-    wins = {}
-    p0 = {}
-    for c in chunks:
-        L = st.chunk_len(c)
-        wins[c] = sorted({0, L - W, int(rng.integers(0, L - W))})
-        p0[c] = [f32_to_host(st.master[c * C + a: c * C + a + W]) for a in wins[c]]
+    assert nc == 30 and st.chunk_len(nc - 1) < C
+    chunks = _first_last_random(nc, np.random.default_rng(wl.seed))
+    p0 = {c: f32_to_host(st.master[c * C: c * C + st.chunk_len(c)]) for c in chunks}
     w = np.full(n, 1.0 / (n * M), np.float32)
     hp = wl.hparams(step=1)
 
@@ -194,21 +176,24 @@ def test_offload_full_size(fuse_last):
     sc = _sc(hp)
     bufs = [torch.empty(C, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
     for c in chunks:
-        print(f"offload: checking chunk {c}", flush=True)
-        L = st.chunk_len(c)
+        L, base = st.chunk_len(c), c * C
         per_mb = []
         for mb in range(M):
             fill.offload_contrib(gen, wl, mb, c, [b[:L] for b in bufs], tmp)
             per_mb.append([bf16_to_host(b[:L]) for b in bufs])
-        for a, p in zip(wins[c], p0[c]):
-            acc = oracle.offload_accumulate([[g[a:a + W] for g in mbg] for mbg in per_mb], w)
-            lo = c * C + a
-            on_host = oracle.offload_accumulate([[g[a:a + W] for g in mbg] for mbg in per_mb[:M - 1]], w) \
+        got = tuple(f32_to_host(x[base:base + L]) for x in (st.master, st.exp_avg, st.exp_avg_sq)) + \
+            (bf16_to_host(st.bf16[base:base + L]),)
+        p = p0[c]
+
+        def work(a, e):
+            acc = oracle.offload_accumulate([[g[a:e] for g in mbg] for mbg in per_mb], w)
+            on_host = oracle.offload_accumulate([[g[a:e] for g in mbg] for mbg in per_mb[:M - 1]], w) \
                 if fuse_last else acc
-            assert_grad_exact(host[lo:lo + W], on_host, f"host shard chunk {c} window {a}")
-            z0 = np.zeros(W, np.float32)
-            ref = oracle.adam_step(p, z0, z0.copy(), acc, sc)
-            assert_state_close(f32_to_host(st.master[lo:lo + W]), f32_to_host(st.exp_avg[lo:lo + W]),
-                               f32_to_host(st.exp_avg_sq[lo:lo + W]), bf16_to_host(st.bf16[lo:lo + W]), ref,
-                               f"chunk {c} window {a}")
+            assert_grad_exact(host[base + a:base + e], on_host, f"host shard chunk {c} [{a}, {e})")
+            z0 = np.zeros(e - a, np.float32)
+            ref = oracle.adam_step(p[a:e], z0, z0.copy(), acc, sc)
+            return assert_state_close(*(x[a:e] for x in got), ref, f"chunk {c} [{a}, {e})")
+
+        print(f"offload (fuse_last={fuse_last}): chunk {c}: {L} elements, max ulp {max_ulps(chunked(L, work))}",
+              flush=True)
     st.engine.close()
