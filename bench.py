@@ -333,11 +333,11 @@ SAMPLE_EVERY = 4   # steps between the sampled per-kernel event pairs
 
 
 def run_flat(args, wl, numels, grad_scales=None, counts=None):
-    """Timed region: args.steps steps bracketed by two events, with an event
-    pair around the 4 owner updates on every SAMPLE_EVERY-th step only: an
-    event between two kernels costs about 10 us of GPU time on this stack, so
-    events around every kernel would add about 3% to the step.  The reduce
-    and all-gather durations come from a separate breakdown pass."""
+    """Timed region: args.steps steps bracketed by two events, with events
+    between the reduce-scatter, the 4 owner updates and the all-gather on
+    every SAMPLE_EVERY-th step only, so that the step time carries few
+    events; the breakdown subtracts the GPU time of one event between two
+    kernels, measured in the same run."""
     import torch
 
     import synthetic as S
@@ -963,42 +963,53 @@ def run_offload(args):
     shard_after = _shard_copy_rates(st.host, 1 << 30)
     link_bytes = 4 * wl.psi * (M + (M - 1) + 1)     # D2H every mb, H2D from mb 2, H2D stream-back
     link_fused = 4 * wl.psi * ((M - 1) + (M - 1))   # the last micro-batch never crosses the link
-    rates = shard_before
-    # The schedule's own bound at the measured pinned-copy rates: micro-batch 1
-    # only copies to the host, micro-batches 2..M copy both ways (at the
-    # bidirectional rate), the stream-back only copies to the device.
+    fresh_after = _pinned_copy_rates(1 << 30)
+    # The schedule at the measured pinned-copy rates: micro-batch 1 only copies
+    # to the host, micro-batches 2..M copy both ways, the stream-back only
+    # copies to the device.  Whether the runtime overlaps the two directions is
+    # not under the application's control (the same process measured them at
+    # the one-way rate and at up to 97 GB/s together), so the schedule is
+    # given at full overlap (the best bidirectional rate measured in this run:
+    # the step's lower bound) and at no overlap (every copy at its one-way rate).
     shard_b = 4 * wl.psi
-    d2h_s, h2d_s = shard_b / (rates["d2h_gbs"] * 1e9), shard_b / (rates["h2d_gbs"] * 1e9)
-    bidir_s = 2 * shard_b / (rates["bidir_gbs"] * 1e9)
+    h2d_gbs = max(r["h2d_gbs"] for r in (shard_before, shard_after, fresh_after))
+    d2h_gbs = max(r["d2h_gbs"] for r in (shard_before, shard_after, fresh_after))
+    best_bidir = max(r["bidir_gbs"] for r in (shard_before, shard_after, fresh_after))
+    d2h_s, h2d_s = shard_b / (d2h_gbs * 1e9), shard_b / (h2d_gbs * 1e9)
+    bidir_s = 2 * shard_b / (best_bidir * 1e9)
     sched_ms = 1e3 * (d2h_s + (M - 1) * bidir_s + h2d_s)
     sched_fused_ms = 1e3 * (d2h_s + (M - 2) * bidir_s + h2d_s)
-    serial_copy_ms = 1e3 * (M * d2h_s + M * h2d_s)
+    serial_ms = 1e3 * (M * d2h_s + M * h2d_s)
+    serial_fused_ms = 1e3 * ((M - 1) * d2h_s + (M - 1) * h2d_s)
     out = _base(wl.description, wl.psi / (ms_step * 1e-3), ms_step, args,
                 {"params": wl.psi, "n_ranks": n, "chunk": C, "micro_batches": M,
                  "step": "M x chunks: reduce into slot c%2 (+H2D of the host chunk from mb 2) and D2H; "
                          "then per chunk H2D + owner Adam"})
+    achieved = link_bytes / (ms_step * 1e-3) / 1e9
     out.update({
         "bound": "host link (PCIe)",
-        "link_gbs": link_bytes / (ms_step * 1e-3) / 1e9,
+        "link_gbs": achieved,
         "link_bytes_per_step": link_bytes,
         "pinned_copy_rates_on_shard_before_steps": shard_before,
         "pinned_copy_rates_on_shard_after_steps": shard_after,
-        "pinned_copy_rates_fresh_buffers_after_steps": _pinned_copy_rates(1 << 30),
-        "schedule_bound_rates": "the shard's own pages, measured before the timed steps",
+        "pinned_copy_rates_fresh_buffers_after_steps": fresh_after,
         "numa_placement": placement,
-        "schedule_bound_ms": sched_ms,
-        "frac_of_schedule_bound": sched_ms / ms_step,
-        "overlap_efficiency": serial_copy_ms / ms_step,
-        "overlap_efficiency_note": "sum of the step's copies each at its one-way rate / step time",
+        "schedule_ms_full_overlap": sched_ms,
+        "schedule_ms_no_overlap": serial_ms,
+        "frac_of_full_overlap_bound": sched_ms / ms_step,
+        "overlap_achieved": (serial_ms - ms_step) / (serial_ms - sched_ms),
+        "overlap_achieved_note": ("where the step lies between the schedule with no overlap of the two copy "
+                                  "directions (0) and with full overlap at the best bidirectional rate (1)"),
         "fused_last_micro_batch": {"ms_per_step": ms_fused, "value": wl.psi / (ms_fused * 1e-3),
                                    "link_bytes_per_step": link_fused,
                                    "link_gbs": link_fused / (ms_fused * 1e-3) / 1e9,
-                                   "schedule_bound_ms": sched_fused_ms,
-                                   "frac_of_schedule_bound": sched_fused_ms / ms_fused},
-        "roofline": {"bound": "link", "achieved": link_bytes / (ms_step * 1e-3) / 1e9,
-                     "peak": rates["bidir_gbs"], "unit": "GB/s",
-                     "frac": (link_bytes / (ms_step * 1e-3) / 1e9) / rates["bidir_gbs"],
-                     "traffic": None, "kernel": "pinned copies (both directions)"},
+                                   "schedule_ms_full_overlap": sched_fused_ms,
+                                   "schedule_ms_no_overlap": serial_fused_ms,
+                                   "frac_of_full_overlap_bound": sched_fused_ms / ms_fused},
+        "roofline": {"bound": "link", "achieved": achieved, "peak": best_bidir, "unit": "GB/s",
+                     "frac": achieved / best_bidir, "traffic": None,
+                     "kernel": "pinned copies (both directions)",
+                     "peak_note": "the best bidirectional pinned-copy rate measured in this run"},
     })
     st.engine.close()
     return out

@@ -310,7 +310,8 @@ int zero_all_gather_layer(const void* const* shards, int n_shards, int64_t shard
  * ([blog] 分片放到 CPU：两个缓冲就够): chunk c of the shard uses slot c % 2.
  *
  * Caller-owned buffers, all given at creation:
- *   host_shard_pinned  FP32[shard_numel] pinned host memory (the accumulator).
+ *   host_shard_pinned  FP32[shard_numel] pinned host memory (hipHostMalloc,
+ *                      or a pinned torch tensor): the accumulator.
  *   slot_contrib[s]    device BF16 buffer of n_ranks*chunk_numel values: rank
  *                      r's contribution to the chunk in slot s starts at
  *                      slot_contrib[s] + r*chunk_numel (a partial last chunk
@@ -345,6 +346,7 @@ int zero_all_gather_layer(const void* const* shards, int n_shards, int64_t shard
  * slot_contrib after the kernel that last read that slot stays the caller's
  * (automatic when both run on one stream).
  * Errors: ZERO_ERR_ARG / ZERO_ERR_ALIGN / ZERO_ERR_SIZE for bad arguments
+ * (ZERO_ERR_ARG also for a host shard that is not pinned host memory)
  * (ZERO_ERR_SIZE also for more than ZERO_OFFLOAD_MAX_CHUNKS chunks: the handle
  * keeps two events per chunk, or when the handle's host memory cannot be
  * allocated), ZERO_ERR_STATE for a chunk out of range, a REDUCE or REDUCE_ADAM

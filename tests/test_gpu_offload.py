@@ -114,6 +114,21 @@ def test_offload_misuse_is_rejected():
     st.engine.reduce(0, 0, w)
     st.sync()
     st.engine.close()
+    # a host shard that is not pinned and mapped for the device (the
+    # device-to-host copy is a kernel writing through that mapping)
+    # (called through the C ABI: the binding itself already refuses it)
+    import ctypes
+    pageable = torch.zeros(4 * 1024, dtype=torch.float32)
+    slots = [torch.zeros(4 * 1024, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    stage = [torch.zeros(1024, device="cuda") for _ in range(2)]
+    handle = ctypes.c_void_p()
+    tables = [(ctypes.c_void_p * 2)(*(t.data_ptr() for t in ts)) for ts in (slots, stage)]
+    status = _lib.load().zero_offload_create(4, pageable.numel(), 1024, pageable.data_ptr(), tables[0],
+                                             tables[1], ctypes.byref(handle))
+    assert status == _lib.ZERO_ERR_ARG and not handle.value
+    assert b"not pinned" in _lib.load().zero_last_error()
+    with pytest.raises(ValueError):
+        z.zero_offload_create(4, pageable.numel(), 1024, pageable, slots, stage)
     # more chunks than a handle may hold (two events per chunk)
     chunk = 16
     host = torch.zeros(_lib.ZERO_OFFLOAD_MAX_CHUNKS * chunk + 1, dtype=torch.float32, pin_memory=True)

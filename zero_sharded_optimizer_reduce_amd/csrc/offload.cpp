@@ -164,6 +164,16 @@ int zero_offload_create(int n_ranks, int64_t shard_numel, int64_t chunk_numel,
     return fail(ZERO_ERR_SIZE, "offload_create: out of host memory");
   }
   hipError_t err = hipGetDevice(&h->device);
+  if (err == hipSuccess) {
+    // pageable memory would turn every asynchronous copy of the shard into a
+    // synchronous one: only pinned host memory (known to the runtime) is taken
+    void* mapped = nullptr;
+    if (hipHostGetDevicePointer(&mapped, host_shard_pinned, 0) != hipSuccess || !mapped) {
+      (void)hipGetLastError();
+      return cleanup(fail(ZERO_ERR_ARG, "offload_create: the host shard is not pinned host memory "
+                                        "(hipHostMalloc or a pinned torch tensor)"));
+    }
+  }
   if (err == hipSuccess) err = hipStreamCreateWithFlags(&h->h2d, hipStreamNonBlocking);
   if (err == hipSuccess) err = hipStreamCreateWithFlags(&h->d2h, hipStreamNonBlocking);
   for (int s = 0; s < 2 && err == hipSuccess; ++s) {
