@@ -936,12 +936,17 @@ def run_offload(args):
         for r, vw in enumerate(views):
             vw.copy_(src[r * C: r * C + vw.numel()])
 
+    step_ms = {}
+
     def timed(fuse_last):
         nonlocal t
+        warm = []
         for _ in range(args.warmup):
             t += 1
+            t0 = time.perf_counter()
             st.step(produce, M, w, wl.hparams(step=t), fuse_last=fuse_last)
             st.sync()
+            warm.append(time.perf_counter() - t0)
         torch.cuda.synchronize()
         times = []
         with no_gc():
@@ -952,6 +957,8 @@ def run_offload(args):
                 st.sync()
                 torch.cuda.synchronize()
                 times.append(time.perf_counter() - t0)
+        step_ms["fused_last" if fuse_last else "literal"] = {"warmup": [1e3 * x for x in warm],
+                                                             "timed": [1e3 * x for x in times]}
         return 1e3 * _mean(times)
 
     torch.cuda.synchronize()
@@ -994,6 +1001,7 @@ def run_offload(args):
         "pinned_copy_rates_on_shard_after_steps": shard_after,
         "pinned_copy_rates_fresh_buffers_after_steps": fresh_after,
         "numa_placement": placement,
+        "step_ms_each": step_ms,
         "schedule_ms_full_overlap": sched_ms,
         "schedule_ms_no_overlap": serial_ms,
         "frac_of_full_overlap_bound": sched_ms / ms_step,
