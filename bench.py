@@ -674,7 +674,9 @@ def run_chain(args):
     del tmp
     SU = CHAIN_SAMPLE_UNIT
 
-    # sampled steps carry events around the kernel groups of layer 16 and of
+    # sampled steps carry events around every layer unit's 4 owner updates
+    # (the roofline kernel, averaged over all 32 layers as a kernel trace
+    # averages it) and around the reduce and the gather of layer 16 and of
     # the embedding (the lm_head has the embedding's size)
     SAMPLED = {SU: "layer", 0: "embedding"}
 
@@ -695,13 +697,16 @@ def run_chain(args):
                 continue
             if rg:
                 ch.forward_unit(u)
-            if sample and u in SAMPLED:
-                a = T.ev()
+            is_layer = 1 <= u <= U - 2
+            if sample and (u in SAMPLED or is_layer):
+                a = T.ev() if u in SAMPLED else None
                 ch.reduce_unit(u, w)
                 b = T.ev()
                 ch.update_unit(u, hp)
-                T.span(SAMPLED[u] + "_rs", a, b)
-                T.span(SAMPLED[u] + "_update4", b, T.ev())
+                c = T.ev()
+                if a is not None:
+                    T.span(SAMPLED[u] + "_rs", a, b)
+                T.span("layer_update4" if is_layer else SAMPLED[u] + "_update4", b, c)
             else:
                 ch.reduce_unit(u, w)
                 ch.update_unit(u, hp)
@@ -737,14 +742,16 @@ def run_chain(args):
     # per-kernel breakdown from the sampled steps' spans, each less the GPU
     # time of one event between two kernels (measured here)
     ev_ms = event_overhead_ms(T, lambda: ch.forward_unit(SU))
-    kern = {"timing": (f"events between the kernel groups of layer 16 and of the embedding on every "
-                       f"{SAMPLE_EVERY}th step of the timed region, each span less the measured GPU time of "
-                       "one event between two kernels; the lm_head is counted with the embedding's figures"),
+    kern = {"timing": (f"events on every {SAMPLE_EVERY}th step of the timed region: around every layer unit's "
+                       "4 owner updates (the layer update is their mean over the 32 layers) and around the "
+                       "reduce and the gather of layer 16 and of the embedding; each span less the measured GPU "
+                       "time of one event between two kernels; the lm_head is counted with the embedding's "
+                       "figures"),
             "event_overhead_ms": ev_ms}
     for name, u, count in (("layer", SU, U - 2), ("embedding", 0, 2)):
         pad, s = ch.units[u][2], ch.units[u][3]
         rs = T.ms(name + "_rs") - ev_ms
-        ad = (T.ms(name + "_update4") - ev_ms) / n
+        ad = (T.ms("layer_update4" if name == "layer" else name + "_update4") - ev_ms) / n
         ag = T.ms(name + "_ag") - ev_ms
         kern[name] = {
             "units_per_step": count, "params_padded": pad, "shard": s,
@@ -776,9 +783,10 @@ def run_chain(args):
                    "peak_allocated_bytes": peak},
         "kernels": kern,
         "roofline": _roofline("adam_shard_step", wl.name, adam_ms, s_lay,
-                              f"HIP events on the launch stream around the 4 owner updates of layer 16 on every "
-                              f"{SAMPLE_EVERY}th step of the timed region, divided by 4 (the span's one event "
-                              "gap is not subtracted here; kernels.layer has the corrected figure)"),
+                              f"HIP events on the launch stream around the 4 owner updates of every layer unit "
+                              f"on every {SAMPLE_EVERY}th step of the timed region: the mean span over the 32 "
+                              "layers, divided by 4 (the span's one event gap is not subtracted here; "
+                              "kernels.layer has the corrected figure)"),
         "fused_variant": {"ms_per_step": f_ms, "value": wl.psi / (f_ms * 1e-3),
                           "step": "backward per unit: fused reduce-scatter + owner update (one launch per "
                                   "owner, the reduced shards kept in registers)",
