@@ -9,7 +9,10 @@
 //   - the all-gather equals a host-side concatenation;
 //   - a zero gradient with zero decay at t = 1 leaves the master weights
 //     unchanged and the moments zero;
-//   - invalid arguments return the documented status and write nothing.
+//   - invalid arguments return the documented status and write nothing;
+//   - the workspace-free gradient norm equals the workspace form bit for bit
+//     on two consecutive calls (the second smaller), and both give the exact
+//     sum of squares of small integers times 2^-10.
 // Built as a shared library and called through one exported function, so the
 // test process runs it without starting another program.
 #include <hip/hip_runtime.h>
@@ -293,6 +296,55 @@ int check_errors(hipStream_t st) {
   return 0;
 }
 
+// Sum of squares of k * 2^-10 for integers |k| <= 50: every square and every
+// partial sum is exact in binary64, so any summation order gives sum(k^2) * 2^-20.
+int norm_case(hipStream_t st, int n_shards, int64_t numel, uint32_t seed) {
+  Dev dev;
+  uint32_t s = seed;
+  const float* shards[ZERO_MAX_RANKS];
+  int64_t ksq = 0;
+  for (int k = 0; k < n_shards; ++k) {
+    std::vector<float> h(numel);
+    for (auto& x : h) {
+      const int kk = static_cast<int>(xorshift(s) % 101u) - 50;
+      x = static_cast<float>(kk) * 0x1p-10f;
+      ksq += static_cast<int64_t>(kk) * kk;
+    }
+    float* d = dev.alloc<float>(numel);
+    if (!d || upload(d, h)) FAIL("upload");
+    shards[k] = d;
+  }
+  double* ws = dev.alloc<double>(static_cast<size_t>(n_shards) * ZERO_NORM_BLOCKS);
+  double* out = dev.alloc<double>(2);
+  float* coef = dev.alloc<float>(2);
+  if (!ws || !out || !coef) FAIL("hipMalloc");
+  ZOK(zero_grad_norm_sq(shards, n_shards, numel, ws, static_cast<int64_t>(n_shards) * ZERO_NORM_BLOCKS, out,
+                        0.5f, coef, st));
+  ZOK(zero_grad_norm_sq_no_alloc(shards, n_shards, numel, out + 1, 0.5f, coef + 1, st));
+  HIPOK(hipStreamSynchronize(st));
+  auto o = download(out, 2);
+  auto c = download(coef, 2);
+  if (o.size() != 2 || c.size() != 2) FAIL("download");
+  if (std::memcmp(&o[0], &o[1], 8) != 0 || std::memcmp(&c[0], &c[1], 4) != 0)
+    FAIL("norm without workspace != with workspace (%d shards of %lld)", n_shards, (long long)numel);
+  if (o[0] != static_cast<double>(ksq) * 0x1p-20)
+    FAIL("norm %.17g != exact %.17g", o[0], static_cast<double>(ksq) * 0x1p-20);
+  return 0;
+}
+
+int check_norm_no_alloc(hipStream_t st) {
+  if (norm_case(st, 3, 4096 * 5 + 4, 4242u)) return 1;   // vector path, several blocks per shard
+  if (norm_case(st, 1, 7, 17u)) return 1;                // smaller: one shard, one block, element tail
+  // too many shards: rejected before anything runs
+  double* out = nullptr;
+  if (hipMalloc(&out, 8) != hipSuccess) FAIL("hipMalloc");
+  const float* many[ZERO_MAX_RANKS + 1] = {};
+  const int s = zero_grad_norm_sq_no_alloc(many, ZERO_MAX_RANKS + 1, 0, out, 0.0f, nullptr, st);
+  (void)hipFree(out);
+  if (s != ZERO_ERR_ARG) FAIL("norm_no_alloc with %d shards: got %d, want ZERO_ERR_ARG", ZERO_MAX_RANKS + 1, s);
+  return 0;
+}
+
 }  // namespace
 
 extern "C" int zero_native_abi_check(char* msg, int msg_len) {
@@ -309,6 +361,7 @@ extern "C" int zero_native_abi_check(char* msg, int msg_len) {
   if (!rc) rc = check_all_gather(st);
   if (!rc) rc = check_zero_gradient(st);
   if (!rc) rc = check_errors(st);
+  if (!rc) rc = check_norm_no_alloc(st);
   if (st) (void)hipStreamDestroy(st);
   if (msg && msg_len > 0) std::snprintf(msg, static_cast<size_t>(msg_len), "%s", rc ? g_msg : "ok");
   return rc;

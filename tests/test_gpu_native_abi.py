@@ -1,8 +1,9 @@
 """The C ABI used from C++ alone (tests/native/abi_gpu_check.cpp): its own
 device buffers and stream, no Python marshalling.  The fused call equals the
 separate calls bit for bit, exact sums come out exact, the all-gather is a
-concatenation, a zero gradient leaves the weights unchanged, and invalid
-arguments return the documented status without writing anything."""
+concatenation, a zero gradient leaves the weights unchanged, invalid
+arguments return the documented status without writing anything, and the
+workspace-free gradient norm equals the workspace form and the exact sum."""
 import ctypes as C
 import os
 
