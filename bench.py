@@ -234,43 +234,56 @@ def _base(workload_desc, value, ms_step, args, extra_cfg=None):
 CPU_SLICE = 1 << 22
 
 
-def _cpu_slice_inputs(kind: str, slice_index: int):
-    """Inputs of one 2^22-parameter slice of a workload, drawn on the host as
-    that workload draws them, and the oracle's weights and step scalars."""
+def _cpu_slice_step(kind: str, slice_index: int):
+    """One oracle step on one 2^22-parameter slice of a workload, its inputs
+    drawn on the host as that workload draws them: returns a callable that
+    runs the step (its results are discarded; the inputs stay as drawn)."""
+    import numpy as np
+
     import oracle
     import synthetic as S
-    from synthetic.workloads import CHAIN_8B, LAYER_7B
+    from synthetic.workloads import CHAIN_8B, LAYER_7B, OFFLOAD_8B, OWNER_8B
 
+    wl = {"layer7b_weighted_adamw": LAYER_7B, "zero3_chain_llama8b": CHAIN_8B,
+          "owner_share_8b_buckets": OWNER_8B, "offload_owner_8b_two_slots": OFFLOAD_8B}[kind]
+    n = wl.n_ranks
+    seed = wl.seed + 1000 * slice_index
+    p, m, v = S.host_state(seed + 1, CPU_SLICE, wl.master_sigma, wl.m_sigma, wl.v_sigma)
+    sc = oracle.adam_scalars(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay, wl.step0)
+    if kind == "owner_share_8b_buckets":
+        # one owner's pre-sliced contributions: the reduce and the owner's update
+        grads = S.host_rank_grads(seed, n, CPU_SLICE, wl.grad_sigma)
+        w = oracle.weights_mean(n)
+        return lambda: oracle.adam_step(p, m, v, oracle.reduce_full(grads, w), sc)
+    if kind == "offload_owner_8b_two_slots":
+        # M micro-batches accumulated, then the owner's update
+        M = wl.extra["micro_batches"]
+        per_mb = [S.host_rank_grads(seed + 7 * mb, n, CPU_SLICE, wl.grad_sigma) for mb in range(M)]
+        w = np.full(n, 1.0 / (n * M), np.float32)
+        return lambda: oracle.adam_step(p, m, v, oracle.offload_accumulate(per_mb, w), sc)
     if kind == "layer7b_weighted_adamw":
-        wl = LAYER_7B
-        seed = wl.seed + 1000 * slice_index
-        grads = S.host_rank_grads(seed, wl.n_ranks, CPU_SLICE, wl.grad_sigma, S.rank_scales(wl.seed, wl.n_ranks))
+        grads = S.host_rank_grads(seed, n, CPU_SLICE, wl.grad_sigma, S.rank_scales(wl.seed, n))
         w = oracle.weights_from_counts(wl.extra["token_counts"])
     else:   # zero3_chain_llama8b: slices of the embedding unit and of layer 0 in turn
-        wl = CHAIN_8B
-        seed = wl.seed + 1000 * slice_index + (0 if slice_index % 2 == 0 else 1)
-        grads = S.host_rank_grads(seed, wl.n_ranks, CPU_SLICE, wl.grad_sigma)
-        w = oracle.weights_mean(wl.n_ranks)
-    p, m, v = S.host_state(seed + 1, CPU_SLICE, wl.master_sigma)
-    sc = oracle.adam_scalars(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay, 1)
-    return wl.n_ranks, grads, w, (p, m, v), sc
+        seed += 0 if slice_index % 2 == 0 else 1
+        grads = S.host_rank_grads(seed, n, CPU_SLICE, wl.grad_sigma)
+        w = oracle.weights_mean(n)
+    s = CPU_SLICE // n
+    shards = [[x[k * s:(k + 1) * s] for k in range(n)] for x in (p, m, v)]
+    return lambda: oracle.sharded_step(grads, w, *shards, sc)
 
 
 def _cpu_slice_worker(kind: str, slice_index: int, target_s: float):
-    """One process: the oracle's sharded step (reduce-scatter, the N owners'
-    updates with the BF16 pack, all-gather) on one 2^22-parameter slice of the
-    workload, repeated until target_s seconds have passed.  Returns
+    """One process: the oracle's step on one 2^22-parameter slice of the
+    workload (for the flat and chain workloads the sharded step: the
+    reduce-scatter, the N owners' updates with the BF16 pack and the
+    all-gather), repeated until target_s seconds have passed.  Returns
     (parameters stepped, seconds)."""
-    import oracle
-
-    n, grads, w, (p, m, v), sc = _cpu_slice_inputs(kind, slice_index)
-    s = CPU_SLICE // n
+    step = _cpu_slice_step(kind, slice_index)
     done = 0
     t0 = time.perf_counter()
     while True:
-        oracle.sharded_step(grads, w, [p[k * s:(k + 1) * s] for k in range(n)],
-                            [m[k * s:(k + 1) * s] for k in range(n)],
-                            [v[k * s:(k + 1) * s] for k in range(n)], sc)
+        step()
         done += CPU_SLICE
         el = time.perf_counter() - t0
         if el >= target_s:
@@ -279,9 +292,17 @@ def _cpu_slice_worker(kind: str, slice_index: int, target_s: float):
 
 CPU_SAMPLES = {
     "layer7b_weighted_adamw": ("2^22-param slices of the 7B-class layer (4 count-weighted BF16 ranks, AdamW "
-                               "wd=0.1)", 202_375_168),
+                               "wd=0.1; the sharded step: reduce-scatter, owner updates with the BF16 pack, "
+                               "all-gather)", 202_375_168),
     "zero3_chain_llama8b": ("2^22-param slices cut alternately from the embedding unit and from layer 0 of the "
-                            "8B chain (4 mean-weighted BF16 ranks, Adam t=1, wd=0)", 8_029_995_008),
+                            "8B chain (4 mean-weighted BF16 ranks, Adam t=1, wd=0; the sharded step: "
+                            "reduce-scatter, owner updates with the BF16 pack, all-gather)", 8_029_995_008),
+    "owner_share_8b_buckets": ("2^22-param slices of the owner's 2.0e9 share (4 mean-weighted BF16 "
+                               "contributions, Adam t=1000 from a mid-run state, wd=0.1; the reduce and the "
+                               "owner's update)", 2_000_000_000),
+    "offload_owner_8b_two_slots": ("2^22-param slices of the offloaded 2.0e9 shard (4 micro-batches of 4 BF16 "
+                                   "contributions at w=1/16 accumulated, then the owner's Adam t=1 update; the "
+                                   "host link is not modelled)", 2_000_000_000),
 }
 
 
@@ -316,8 +337,8 @@ def cpu_baseline(kind: str, target_s: float):
         pass
     rate, rate1 = done_all / wall, done1 / el1
     return {"value": rate, "unit": "params/s", "cores": cores, "kind": "oracle",
-            "sample": (f"oracle sharded step (reduce-scatter, owner updates with the BF16 pack, all-gather) on "
-                       f"{what}: {cores} processes, one slice each, {done_all // CPU_SLICE} slice-steps, the "
+            "sample": (f"the oracle's step on {what}: {cores} processes, one slice each, "
+                       f"{done_all // CPU_SLICE} slice-steps, the "
                        f"slowest process's loop {wall:.1f} s; numpy ufuncs, one thread per process; {model}, "
                        f"{os.cpu_count()} CPUs visible, {cores} in the affinity mask used (capped at 16). "
                        f"Extrapolated by parameter count: one {psi:,}-parameter step would take "
@@ -639,6 +660,21 @@ def run_owner_share(args):
 
 
 # --------------------------------------------------------------------------- ZeRO-3 chain
+def _fused_kernel_entry(T, n, shard, regather):
+    """The fused kernel on a layer unit: mean launch time over the sampled
+    spans around every layer unit's 4 owner launches (the gather that
+    regather adds is inside the span, so then only the span is given)."""
+    ms = T.ms("layer_fused4")
+    if regather or ms <= 0:
+        return {"span_ms": ms}
+    launch = ms / n
+    b = (2 * n + 26) * shard
+    return {"ms": launch, "bytes": b, "gbs": b / (launch * 1e-3) / 1e9,
+            "frac_of_peak": b / (launch * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "timing": f"HIP events around every layer unit's 4 fused launches on every {SAMPLE_EVERY}th step, "
+                      "mean over the 32 layers, divided by 4"}
+
+
 CHAIN_SAMPLE_UNIT = 17   # layer 16 (unit 0 is the embedding, unit 33 the lm_head)
 
 
@@ -693,7 +729,12 @@ def run_chain(args):
             mid.append(T.ev())
         for u in reversed(range(U)):            # backward
             if fused:
-                ch.backward_unit_fused(u, w, hp, regather=rg)
+                if sample and 1 <= u <= U - 2:
+                    a = T.ev()
+                    ch.backward_unit_fused(u, w, hp, regather=rg)
+                    T.span("layer_fused4", a, T.ev())
+                else:
+                    ch.backward_unit_fused(u, w, hp, regather=rg)
                 continue
             if rg:
                 ch.forward_unit(u)
@@ -791,7 +832,8 @@ def run_chain(args):
                           "step": "backward per unit: fused reduce-scatter + owner update (one launch per "
                                   "owner, the reduced shards kept in registers)",
                           "hbm_gbs_algorithmic": (2 * n + 26 + B_AG * (2 if rg else 1)) * psi_pad
-                          / (f_ms * 1e-3) / 1e9},
+                          / (f_ms * 1e-3) / 1e9,
+                          "fused_kernel_layer": _fused_kernel_entry(T, n, s_lay, rg)},
     })
     del ch
     gc.collect()

@@ -20,7 +20,9 @@ def test_more_than_one_gpu_is_refused():
 
 
 @pytest.mark.parametrize("kind, psi", [("zero3_chain_llama8b", 8_029_995_008),
-                                       ("layer7b_weighted_adamw", 202_375_168)])
+                                       ("layer7b_weighted_adamw", 202_375_168),
+                                       ("owner_share_8b_buckets", 2_000_000_000),
+                                       ("offload_owner_8b_two_slots", 2_000_000_000)])
 def test_cpu_baseline_fields(kind, psi):
     sys.path.insert(0, ROOT)
     import bench
