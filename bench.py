@@ -169,9 +169,6 @@ class Timer:
     def ms(self, name):
         return _mean([a.elapsed_time(b) for a, b in self.spans.get(name, [])])
 
-    def total_ms(self, name):
-        return float(sum(a.elapsed_time(b) for a, b in self.spans.get(name, [])))
-
 
 def event_overhead_ms(T, fn, reps=20, rounds=3):
     """GPU time that one event recorded between two kernels adds to the
