@@ -54,12 +54,10 @@ B_ADAM = 30                     # read g, p, m, v (16 B); write p, m, v (12 B) +
 B_AG = 4                        # read and write one BF16 value
 
 
-def _elf_section(path: str, name: str) -> bytes:
-    """The bytes of section `name` of a little-endian ELF64 file."""
-    with open(path, "rb") as f:
-        d = f.read()
+def _elf_section_bytes(d: bytes, name: str, what: str = "ELF") -> bytes:
+    """The bytes of section `name` of a little-endian ELF64 image."""
     if d[:4] != b"\x7fELF" or d[4] != 2:
-        raise ValueError(f"{path} is not an ELF64 file")
+        raise ValueError(f"{what} is not an ELF64 image")
     shoff, = struct.unpack_from("<Q", d, 0x28)
     shentsize, shnum, shstrndx = struct.unpack_from("<HHH", d, 0x3A)
 
@@ -72,16 +70,44 @@ def _elf_section(path: str, name: str) -> bytes:
         nm, off, size = header(i)
         if d[strtab + nm: d.index(b"\0", strtab + nm)] == name.encode():
             return d[off:off + size]
-    raise ValueError(f"{path} has no {name} section")
+    raise ValueError(f"{what} has no {name} section")
+
+
+def _elf_section(path: str, name: str) -> bytes:
+    with open(path, "rb") as f:
+        return _elf_section_bytes(f.read(), name, path)
 
 
 def device_code_hash() -> str:
-    """sha256 of the device code that libzero.so carries (its .hip_fatbin
-    section: every gfx950 code object of the library).  Builds are
-    deterministic and edits that leave the machine code alone (comments,
-    host code) keep the hash, so a stored counter reading stays valid exactly
-    as long as the kernels it measured are the ones that run."""
-    return hashlib.sha256(_elf_section(LIBZERO, ".hip_fatbin")).hexdigest()
+    """sha256 of the machine code libzero.so carries for the GPU: for every
+    amdgcn code object in its .hip_fatbin section (clang offload bundles), the
+    .text section (the instructions) and the .rodata section (the kernel
+    descriptors: resources, LDS, entry offsets).  Symbol and string tables
+    are left out: they carry compilation-unit IDs derived from the source
+    path, so the same sources built in another directory keep the hash, and
+    so do edits that leave the machine code alone (comments, host code)."""
+    fat = _elf_section(LIBZERO, ".hip_fatbin")
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    h = hashlib.sha256()
+    objects = 0
+    pos = fat.find(magic)
+    while pos >= 0:
+        count, = struct.unpack_from("<Q", fat, pos + len(magic))
+        q = pos + len(magic) + 8
+        for _ in range(count):
+            off, size, tlen = struct.unpack_from("<QQQ", fat, q)
+            triple = fat[q + 24:q + 24 + tlen]
+            q += 24 + tlen
+            if b"amdgcn" in triple:
+                co = fat[pos + off:pos + off + size]
+                h.update(triple)
+                for sec in (".text", ".rodata"):
+                    h.update(_elf_section_bytes(co, sec, triple.decode(errors="replace")))
+                objects += 1
+        pos = fat.find(magic, pos + len(magic))
+    if objects == 0:
+        raise ValueError(f"{LIBZERO} carries no amdgcn code object")
+    return h.hexdigest()
 
 
 def _traffic(kernel: str, workload: str, launch_params: int):
