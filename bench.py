@@ -11,10 +11,11 @@ shards are all-gathered into a temporary view, which is released.  Backward,
 units in reverse order: reduce-scatter of the 4 ranks' BF16 contributions
 into 4 FP32 owner shards, then the 4 owners' fused Adam updates (FP32 master,
 m, v and the BF16 working shard).  Inputs are resident in HBM before the timed
-region.  The same line carries the 7B-class layer figures (d=4096,
-ffn=11008, 202,375,168 parameters, ranks weighted by token counts, AdamW
-wd=0.1) under an extra key, measured in a child process that runs before this
-process touches the GPU.
+region.  The same line carries, under extra keys, the figures of the
+7B-class layer (d=4096, ffn=11008, 202,375,168 parameters, ranks weighted by
+token counts, AdamW wd=0.1), of one owner's 2.0e9-parameter share in 64M
+buckets and of the host-offloaded shard, each measured in a child process
+that runs before this process touches the GPU (--chain-only leaves them out).
 
 Other workloads (--workload): tiny_flat_1m, layer7b_weighted_adamw,
 owner_share_8b_buckets (one owner's 2.0e9-parameter share in 64M buckets),
@@ -1146,14 +1147,25 @@ def _nested(result):
     return {k: v for k, v in result.items() if k not in drop}
 
 
-def _child_workload(name, args):
+# The other workloads' figures carried by the default line, each from a child
+# process: (steps, warmup) as functions of the line's own.
+EXTRA_WORKLOADS = {
+    "layer7b_weighted_adamw": lambda steps, warmup: (steps, warmup),
+    "owner_share_8b_buckets": lambda steps, warmup: (steps, min(warmup, 3)),
+    "offload_owner_8b_two_slots": lambda steps, warmup: (min(steps, 3), 1),
+}
+
+
+def _child_workload(name, args, steps=None, warmup=None):
     """Run one workload of this script in a child process and return its line
     (as an extra key).  Started before this process touches the GPU, so the
     two never use it at once and the child's buffers are its own fresh
     allocations; the child's progress lines go to stderr as they come."""
     import subprocess
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     cmd = [sys.executable, os.path.abspath(__file__), "--workload", name, "--no-cpu-baseline",
-           "--steps", str(args.steps), "--warmup", str(args.warmup)]
+           "--steps", str(steps), "--warmup", str(warmup)]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=900)
     lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
     if r.returncode != 0 or not lines:
@@ -1171,8 +1183,9 @@ def main():
     ap.add_argument("--workload", default="zero3_chain_llama8b", choices=sorted(RUNNERS))
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-layer7b", action="store_true",
-                    help="zero3_chain_llama8b: leave out the 7B-class layer figures that follow the chain")
+    ap.add_argument("--chain-only", "--no-layer7b", dest="chain_only", action="store_true",
+                    help="zero3_chain_llama8b: leave out the other workloads' figures (7B-class layer, owner "
+                         "share, offload) that the line carries")
     ap.add_argument("--regather-bwd", action="store_true",
                     help="zero3_chain_llama8b: gather each unit again before its backward reduce")
     args = ap.parse_args()
@@ -1183,10 +1196,12 @@ def main():
     cpu = None
     if args.workload in CPU_SAMPLES and not args.no_cpu_baseline:
         cpu = cpu_baseline(args.workload, args.cpu_baseline_seconds)    # before anything touches the GPU
-    layer = None
-    if args.workload == "zero3_chain_llama8b" and not args.no_layer7b:
-        print("bench: 7B-class layer figures (child process)", file=sys.stderr, flush=True)
-        layer = _child_workload("layer7b_weighted_adamw", args)
+    extras = {}
+    if args.workload == "zero3_chain_llama8b" and not args.chain_only:
+        for name, shape in EXTRA_WORKLOADS.items():
+            steps, warmup = shape(args.steps, args.warmup)
+            print(f"bench: {name} figures (child process)", file=sys.stderr, flush=True)
+            extras[name] = _child_workload(name, args, steps, warmup)
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -1201,8 +1216,7 @@ def main():
     out = RUNNERS[args.workload](args)
     if cpu is not None:
         out["cpu_baseline"] = cpu
-    if layer is not None:
-        out["layer7b_weighted_adamw"] = layer
+    out.update(extras)
     print(json.dumps(out), flush=True)
 
 
