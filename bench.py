@@ -114,7 +114,8 @@ def device_code_hash() -> str:
 def _traffic(kernel: str, workload: str, launch_params: int):
     """(HBM bytes per launch, source note) of `kernel` from the committed
     rocprofv3 counter summary, or (None, reason) if there is none, or the
-    kernel sources changed since it was taken, or it covers another size."""
+    library's device code has changed since it was taken, or it covers
+    another launch size."""
     name = f"{kernel}_{workload}_traffic.txt"
     path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
