@@ -94,3 +94,25 @@ def test_child_workload_failure_is_reported_not_raised():
     import bench
     out = bench._child_workload("layer7b_weighted_adamw", argparse.Namespace(steps=1, warmup=0))
     assert "error" in out and "exited with 1" in out["error"]
+
+
+def test_committed_traffic_summaries_match_the_built_device_code(libzero):
+    # the bench line reports roofline.traffic from these files only while the
+    # library carries the machine code their counters were taken on: a kernel
+    # change without new counter passes would turn the field into null
+    import glob
+
+    import bench
+    code = bench.device_code_hash()
+    files = sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.txt")))
+    assert files
+    for path in files:
+        kv = {}
+        for line in open(path):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        assert kv["device_code_sha256"] == code, os.path.basename(path)
+        ratio = float(kv["hbm_bytes_per_launch"]) / float(kv["algorithmic_bytes_per_launch"])
+        assert ratio == pytest.approx(float(kv["traffic_over_algorithmic"]), abs=1e-6)
+        assert 0.999 < ratio < 1.001, os.path.basename(path)
