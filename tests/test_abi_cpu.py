@@ -69,6 +69,23 @@ def test_rank_weights_and_layout_match_oracle(libzero):
         assert api.zero_shard_layout(numels, n) == oracle.shard_layout(numels, n)
 
 
+def test_rank_weights_argument_errors(libzero):
+    from zero_sharded_optimizer_reduce_amd import api
+    from zero_sharded_optimizer_reduce_amd._lib import ZeroError
+    with pytest.raises(ValueError, match="len"):
+        api.zero_rank_weights([1, 2, 3], 2)          # more counts than ranks
+    with pytest.raises(ValueError, match="len"):
+        api.zero_rank_weights([1], 2)
+    with pytest.raises(ValueError, match="at least 1"):
+        api.zero_rank_weights(None, 0)
+    with pytest.raises(ZeroError):
+        api.zero_rank_weights(None, 17)              # the C ABI's limit
+    with pytest.raises(ZeroError):
+        api.zero_rank_weights([0, 0], 2)             # counts summing to 0
+    with pytest.raises(ZeroError):
+        api.zero_rank_weights([3, -1], 2)
+
+
 def _pp(*vals):
     return (C.c_void_p * len(vals))(*vals)
 

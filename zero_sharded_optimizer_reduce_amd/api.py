@@ -61,10 +61,12 @@ def zero_adam_scalars_compute(hp) -> dict:
 
 
 def zero_rank_weights(counts: Optional[Sequence[int]], n_ranks: int) -> np.ndarray:
-    out = (C.c_float * n_ranks)()
-    arr = None if counts is None else (C.c_int64 * n_ranks)(*[int(c) for c in counts])
     if counts is not None and len(counts) != n_ranks:
         raise ValueError("zero_rank_weights: len(counts) != n_ranks")
+    if n_ranks < 1:
+        raise ValueError("zero_rank_weights: n_ranks must be at least 1")
+    out = (C.c_float * n_ranks)()
+    arr = None if counts is None else (C.c_int64 * n_ranks)(*[int(c) for c in counts])
     check(load().zero_rank_weights(arr, n_ranks, out), "zero_rank_weights")
     return np.array(list(out), dtype=np.float32)
 
@@ -244,7 +246,7 @@ def adam_scalars_tensor(hp, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     if out is None:
         return torch.tensor(vals, dtype=torch.float32)
     if out.device.type != "cpu" or out.dtype != torch.float32 or out.numel() < ADAM_SCALARS_FLOATS:
-        raise ValueError("adam_scalars_tensor: out must be a CPU float32 tensor of >= 9 elements")
+        raise ValueError(f"adam_scalars_tensor: out must be a CPU float32 tensor of >= {ADAM_SCALARS_FLOATS} elements")
     out.numpy()[:ADAM_SCALARS_FLOATS] = np.array(vals, dtype=np.float32)
     return out
 
