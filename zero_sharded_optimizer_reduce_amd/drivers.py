@@ -167,9 +167,10 @@ class Zero3Chain:
     """ZeRO-3 per-unit chain: every unit's weights live only as N BF16 owner
     shards (plus FP32 master/m/v per owner).  Forward: for each unit in order,
     all-gather the shards into a temporary full view, then release it.
-    Backward: for each unit in reverse order, the caller's producer writes N
-    BF16 gradient contributions, which are reduce-scattered and applied by each
-    owner's update."""
+    Backward: for each unit in reverse order, the caller writes the unit's N
+    BF16 gradient contributions into `grads` (the first units[u] padded
+    elements of each), which are reduce-scattered and applied by each owner's
+    update."""
 
     def __init__(self, units, n_ranks: int, device="cuda"):
         self.n = n_ranks
