@@ -168,9 +168,9 @@ class Zero3Chain:
     shards (plus FP32 master/m/v per owner).  Forward: for each unit in order,
     all-gather the shards into a temporary full view, then release it.
     Backward: for each unit in reverse order, the caller writes the unit's N
-    BF16 gradient contributions into `grads` (the first units[u][2]
-    elements of each: the unit's padded length), which are reduce-scattered and applied by each owner's
-    update."""
+    BF16 gradient contributions into `grads` (the first units[u][2] elements
+    of each: the unit's padded length); they are reduce-scattered and applied
+    by each owner's update."""
 
     def __init__(self, units, n_ranks: int, device="cuda"):
         self.n = n_ranks
