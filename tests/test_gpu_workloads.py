@@ -1,19 +1,19 @@
-"""GPU parity at full size, in the launch configuration bench.py times, on
-whole sampled units that the oracle recomputes on the host, every element
-compared (the reduced gradients bit for bit, the state at ulp distance 0):
+"""GPU parity at full size, in the launch configuration bench.py times, every
+element of every output compared with the oracle recomputed on the host (the
+reduced gradients bit for bit, the state at ulp distance 0):
 
 * one owner's 2.0e9-parameter share updated in 30 buckets of 2^26 (t=1000,
-  wd=0.1): the first bucket, the partial last bucket and 3 seeded random
-  buckets;
-* the ZeRO-3 chain over the 8B Llama-like model's 34 units: the embedding,
-  the lm_head and 3 seeded random layers: their gathered views, reduced
-  gradients and updated state;
+  wd=0.1): every bucket, the partial last one included;
+* one step of the ZeRO-3 chain over the 8B Llama-like model's 34 units:
+  every gathered view, and every unit's reduced gradients and updated state;
 * the host-offloaded 2.0e9-parameter gradient shard through two slots over 4
-  micro-batches: the first chunk, the partial last chunk and 3 seeded random
-  chunks, both the host accumulation and the updated state.
+  micro-batches: every chunk, the partial last one included, both the host
+  accumulation and the updated state.
 
-Inputs are drawn on the device with keyed generators (synthetic.fill) and the
-checked units are copied to the host (or regenerated from their keys)."""
+Inputs are drawn on the device with keyed generators (synthetic.fill); each
+unit, bucket or chunk is copied to the host (or its inputs regenerated from
+their keys) just before or after the GPU updates it, so host memory holds one
+at a time."""
 import gc
 
 import numpy as np
@@ -37,11 +37,6 @@ def _sc(hp):
     return oracle.adam_scalars(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"], hp["step"])
 
 
-def _first_last_random(n, rng, k=3):
-    """Indices 0 and n-1 and k seeded random ones between them."""
-    return [0, n - 1] + sorted(int(x) for x in rng.choice(np.arange(1, n - 1), k, replace=False))
-
-
 @pytest.fixture(autouse=True)
 def _free_memory():
     yield
@@ -60,29 +55,23 @@ def test_owner_share_buckets_full_size():
     del tmp
     nb = len(st.bounds)
     assert nb == 30 and st.bounds[-1][1] - st.bounds[-1][0] == wl.psi - 29 * BUCKET
-    picks = _first_last_random(nb, np.random.default_rng(wl.seed))
+    # the inputs were drawn from keys: regenerating one bucket gives the same values
+    lo, hi = st.bounds[7]
+    assert torch.equal(fill.owner_share_region(gen, wl, "v", lo, hi), st.exp_avg_sq[lo:hi])
     w = z.zero_rank_weights(None, n)
     hp = wl.hparams(step=wl.step0)
-    pre = {}
-    for b in picks:
-        lo, hi = st.bounds[b]
-        print(f"owner share: bucket {b} [{lo}, {hi})", flush=True)
-        # the reduced gradient of the bucket, as the step computes it (the
-        # step's own bucket buffer is reused, so it is taken here)
-        red = torch.empty(hi - lo, dtype=torch.float32, device="cuda")
-        z.zero_reduce_scatter([c[lo:hi] for c in st.contrib], w, [red])
-        pre[b] = ([bf16_to_host(c[lo:hi]) for c in st.contrib], f32_to_host(st.master[lo:hi]),
-                  f32_to_host(st.exp_avg[lo:hi]), f32_to_host(st.exp_avg_sq[lo:hi]), f32_to_host(red))
-        del red
-    # the inputs were drawn from keys: regenerating one bucket gives the same values
-    lo, hi = st.bounds[picks[2]]
-    assert np.array_equal(f32_to_host(fill.owner_share_region(gen, wl, "v", lo, hi)), pre[picks[2]][3])
-    st.step(w, hp)
-    torch.cuda.synchronize()
     sc = _sc(hp)
-    for b in picks:
+    worst = ((0, 0, 0), 0)
+    # the step bucket by bucket (step() is this loop): each bucket's inputs are
+    # taken just before its update, its reduced gradient from the step's own
+    # bucket buffer just after
+    for b in range(nb):
         lo, hi = st.bounds[b]
-        g, p, m, v, gpu_red = pre[b]
+        g = [bf16_to_host(c[lo:hi]) for c in st.contrib]
+        p, m, v = (f32_to_host(x[lo:hi]) for x in (st.master, st.exp_avg, st.exp_avg_sq))
+        st.step_bucket(b, w, hp)
+        torch.cuda.synchronize()
+        gpu_red = f32_to_host(st.grad_bucket[: hi - lo])
         got = (f32_to_host(st.master[lo:hi]), f32_to_host(st.exp_avg[lo:hi]), f32_to_host(st.exp_avg_sq[lo:hi]),
                bf16_to_host(st.bf16[lo:hi]))
 
@@ -92,10 +81,20 @@ def test_owner_share_buckets_full_size():
             ref = oracle.adam_step(p[a:e], m[a:e], v[a:e], red, sc)
             return assert_state_close(*(x[a:e] for x in got), ref, f"bucket {b} [{a}, {e})")
 
-        print(f"owner share: bucket {b}: {hi - lo} elements, max ulp {max_ulps(chunked(hi - lo, work))}", flush=True)
+        u = max_ulps(chunked(hi - lo, work))
+        worst = max_ulps([worst, u])
+        print(f"owner share: bucket {b} [{lo}, {hi}): max ulp {u}", flush=True)
+        del g, p, m, v, gpu_red, got
+    print(f"owner share: all {nb} buckets, {wl.psi} elements, max ulp {worst}", flush=True)
 
 
-def test_zero3_chain_full_size():
+CHAIN_GROUPS = 5   # the backward's 34 units in 5 tests of 6-7 units each, in backward order
+
+
+@pytest.fixture(scope="module")
+def chain8b():
+    """The 8B chain's buffers (112 GB of owner state), filled once for the
+    forward test and the backward groups of this module."""
     wl = CHAIN_8B
     n = wl.n_ranks
     ch = Zero3Chain(wl.extra["units"], n, device="cuda")
@@ -105,39 +104,56 @@ def test_zero3_chain_full_size():
         fill.fill_normal_pieces(gen, ch.master[k], wl.master_sigma, fill.K_MASTER + 100 * k)
         for lo, hi in fill.pieces(ch.owner_numel):
             ch.bf16[k][lo:hi].copy_(ch.master[k][lo:hi])
-    U = len(ch.units)
-    sampled = _first_last_random(U, np.random.default_rng(wl.seed))
+    yield ch, gen
+    del ch
+    gc.collect()
+    torch.cuda.empty_cache()
 
-    def flat(bufs, u, host=f32_to_host):
-        """Unit u of per-owner buffers as one flat array in owner order."""
-        s, off = ch.units[u][3], ch.offsets[u]
-        return np.concatenate([host(b[off:off + s]) for b in bufs])
 
-    pre = {u: flat(ch.master, u) for u in sampled}        # m = v = 0 before the first step
-    w = z.zero_rank_weights(None, n)
-    hp = wl.hparams(step=1)
-    tmp = torch.empty(ch.max_pad, dtype=torch.float32, device="cuda")
-    # forward: gather each unit into the temporary view, check sampled views, release
+def _unit_flat(ch, bufs, u, host=f32_to_host):
+    """Unit u of per-owner buffers as one flat array in owner order."""
+    s, off = ch.units[u][3], ch.offsets[u]
+    return np.concatenate([host(b[off:off + s]) for b in bufs])
+
+
+def test_zero3_chain_full_size_forward(chain8b):
+    """Forward: every unit gathered into the temporary view, checked, released."""
+    ch, _ = chain8b
+    n, U = ch.n, len(ch.units)
     for u in range(U):
         view = ch.forward_unit(u)
-        if u in sampled:
-            torch.cuda.synchronize()
-            print(f"chain: view of unit {u} ({ch.units[u][0]}, {ch.units[u][2]} elements)", flush=True)
-            assert np.array_equal(bf16_to_host(view), oracle.all_gather(
-                [bf16_to_host(ch.bf16[k][ch.offsets[u]:ch.offsets[u] + ch.units[u][3]]) for k in range(n)])), u
-    # backward in reverse order
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_to_host(view), oracle.all_gather(
+            [bf16_to_host(ch.bf16[k][ch.offsets[u]:ch.offsets[u] + ch.units[u][3]]) for k in range(n)])), u
+    print(f"chain: all {U} gathered views equal the concatenated owner shards", flush=True)
+
+
+@pytest.mark.parametrize("group", range(CHAIN_GROUPS))
+def test_zero3_chain_full_size_backward(chain8b, group):
+    """Backward, units in reverse order (this group's share of them): every
+    unit's reduced gradients and updated state, each unit's master taken just
+    before its update (m = v = 0 before the first step)."""
+    ch, gen = chain8b
+    wl = CHAIN_8B
+    n, U = ch.n, len(ch.units)
+    order = list(reversed(range(U)))
+    per = -(-U // CHAIN_GROUPS)
+    units = order[group * per:(group + 1) * per]
+    w = z.zero_rank_weights(None, n)
+    hp = wl.hparams(step=1)
     sc = _sc(hp)
-    for u in reversed(range(U)):
+    tmp = torch.empty(ch.max_pad, dtype=torch.float32, device="cuda")
+    worst = ((0, 0, 0), 0)
+    for u in units:
         pad, s = ch.units[u][2], ch.units[u][3]
+        p0 = _unit_flat(ch, ch.master, u)
         fill.chain_unit_grads(gen, wl, u, ch.grads, pad, tmp)
         ch.backward_unit(u, w, hp)
-        if u not in sampled:
-            continue
         torch.cuda.synchronize()
         g = [bf16_to_host(x[:pad]) for x in ch.grads]
         gpu_red = np.concatenate([f32_to_host(x[:s]) for x in ch.grad_shards])
-        got = (flat(ch.master, u), flat(ch.exp_avg, u), flat(ch.exp_avg_sq, u), flat(ch.bf16, u, bf16_to_host))
-        p0 = pre.pop(u)
+        got = tuple(_unit_flat(ch, b, u) for b in (ch.master, ch.exp_avg, ch.exp_avg_sq)) + \
+            (_unit_flat(ch, ch.bf16, u, bf16_to_host),)
 
         def work(a, e):
             red = oracle.reduce_full([x[a:e] for x in g], w)
@@ -146,9 +162,11 @@ def test_zero3_chain_full_size():
             ref = oracle.adam_step(p0[a:e], z0, z0.copy(), red, sc)
             return assert_state_close(*(x[a:e] for x in got), ref, f"unit {u} [{a}, {e})")
 
-        print(f"chain: unit {u} ({ch.units[u][0]}): {pad} elements, max ulp {max_ulps(chunked(pad, work))}",
-              flush=True)
+        ulps = max_ulps(chunked(pad, work))
+        worst = max_ulps([worst, ulps])
+        print(f"chain: unit {u} ({ch.units[u][0]}): {pad} elements, max ulp {ulps}", flush=True)
         del g, gpu_red, got, p0
+    print(f"chain: units {units[0]}..{units[-1]}, max ulp {worst}", flush=True)
 
 
 @pytest.mark.parametrize("fuse_last", [False, True])
@@ -161,8 +179,7 @@ def test_offload_full_size(fuse_last):
     fill.fill_normal_pieces(gen, st.master, wl.master_sigma, fill.K_MASTER)
     nc = st.n_chunks
     assert nc == 30 and st.chunk_len(nc - 1) < C
-    chunks = _first_last_random(nc, np.random.default_rng(wl.seed))
-    p0 = {c: f32_to_host(st.master[c * C: c * C + st.chunk_len(c)]) for c in chunks}
+    p0 = f32_to_host(st.master)                    # m = v = 0 before the first step
     w = np.full(n, 1.0 / (n * M), np.float32)
     hp = wl.hparams(step=1)
 
@@ -175,7 +192,8 @@ def test_offload_full_size(fuse_last):
     host = st.host.numpy()
     sc = _sc(hp)
     bufs = [torch.empty(C, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
-    for c in chunks:
+    worst = ((0, 0, 0), 0)
+    for c in range(nc):
         L, base = st.chunk_len(c), c * C
         per_mb = []
         for mb in range(M):
@@ -183,7 +201,7 @@ def test_offload_full_size(fuse_last):
             per_mb.append([bf16_to_host(b[:L]) for b in bufs])
         got = tuple(f32_to_host(x[base:base + L]) for x in (st.master, st.exp_avg, st.exp_avg_sq)) + \
             (bf16_to_host(st.bf16[base:base + L]),)
-        p = p0[c]
+        p = p0[base:base + L]
 
         def work(a, e):
             acc = oracle.offload_accumulate([[g[a:e] for g in mbg] for mbg in per_mb], w)
@@ -194,6 +212,9 @@ def test_offload_full_size(fuse_last):
             ref = oracle.adam_step(p[a:e], z0, z0.copy(), acc, sc)
             return assert_state_close(*(x[a:e] for x in got), ref, f"chunk {c} [{a}, {e})")
 
-        print(f"offload (fuse_last={fuse_last}): chunk {c}: {L} elements, max ulp {max_ulps(chunked(L, work))}",
-              flush=True)
+        ulps = max_ulps(chunked(L, work))
+        worst = max_ulps([worst, ulps])
+        print(f"offload (fuse_last={fuse_last}): chunk {c}: {L} elements, max ulp {ulps}", flush=True)
+        del per_mb, got
+    print(f"offload (fuse_last={fuse_last}): all {nc} chunks, {wl.psi} elements, max ulp {worst}", flush=True)
     st.engine.close()
