@@ -137,15 +137,16 @@ int zero_reduce_scatter(const uint16_t* const* rank_grads, const float* rank_wei
                     "zero_reduce_scatter");
 }
 
-static int adam_common(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* bf16_out,
-                       const float* grad, const float* grad_scale, int64_t n,
-                       const zero_adam_hparams* hp, void* stream, const char* where) {
-  Err e;
-  int st = check_adam(master, exp_avg, exp_avg_sq, bf16_out, grad, n, hp, e);
-  if (st) return fail(st, e.msg);
+// The update once its buffers (and hyper-parameters or device scalars) are
+// checked: the optional gradient scale's checks, then the launch with the host
+// scalars `s` or, when sdev is given, the device struct read when it runs.
+static int adam_checked(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* bf16_out, const float* grad,
+                        const float* grad_scale, int64_t n, const zero_adam_scalars& s,
+                        const zero_adam_scalars* sdev, void* stream, const char* where) {
   if (n == 0) return ZERO_OK;
   if (grad_scale) {
-    st = check_adam_scale(grad_scale, master, exp_avg, exp_avg_sq, bf16_out, n, e);
+    Err e;
+    int st = check_adam_scale(grad_scale, master, exp_avg, exp_avg_sq, bf16_out, n, e);
     if (st) return fail(st, e.msg);
   }
   AdamParams a;
@@ -157,11 +158,24 @@ static int adam_common(float* master, float* exp_avg, float* exp_avg_sq, uint16_
   a.g = grad;
   a.gscale = grad_scale;
   a.n = n;
-  adam_scalars(hp, &a.s, e);
+  a.s = s;
+  a.sdev = sdev;
   const bool vec = aligned16(master) && aligned16(exp_avg) && aligned16(exp_avg_sq) &&
                    aligned16(grad) && aligned8(bf16_out);
   set_path(vec);
   return hip_status(launch_adam(a, vec, static_cast<hipStream_t>(stream)), where);
+}
+
+static int adam_common(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* bf16_out,
+                       const float* grad, const float* grad_scale, int64_t n,
+                       const zero_adam_hparams* hp, void* stream, const char* where) {
+  Err e;
+  int st = check_adam(master, exp_avg, exp_avg_sq, bf16_out, grad, n, hp, e);
+  if (st) return fail(st, e.msg);
+  zero_adam_scalars sc;
+  memset(&sc, 0, sizeof sc);
+  adam_scalars(hp, &sc, e);
+  return adam_checked(master, exp_avg, exp_avg_sq, bf16_out, grad, grad_scale, n, sc, nullptr, stream, where);
 }
 
 int zero_reduce_scatter_f32(const float* const* rank_grads, const float* rank_weights, int n_ranks,
@@ -209,19 +223,20 @@ int zero_adam_shard_step_scaled(float* master, float* exp_avg, float* exp_avg_sq
                      "zero_adam_shard_step_scaled");
 }
 
-int zero_grad_norm_sq(const float* const* shards, int n_shards, int64_t shard_numel,
-                      double* workspace, int64_t workspace_len, double* norm_sq_out,
-                      float max_norm, float* clip_coef_out, void* stream) {
-  TraceRange tr("zero_grad_norm_sq");
+// Both norm entry points: checks, then the two norm launches with `partials`
+// (a caller workspace of workspace_len doubles, or the library's own array).
+static int norm_common(const float* const* shards, int n_shards, int64_t shard_numel, double* partials,
+                       int64_t partials_len, double* norm_sq_out, float max_norm, float* clip_coef_out,
+                       void* stream, const char* where) {
   Err e;
-  int st = check_grad_norm(shards, n_shards, shard_numel, workspace, workspace_len, norm_sq_out,
-                           max_norm, clip_coef_out, e);
+  int st = check_grad_norm(shards, n_shards, shard_numel, partials, partials_len, norm_sq_out, max_norm,
+                           clip_coef_out, e);
   if (st) return fail(st, e.msg);
   NormParams p;
   memset(&p, 0, sizeof p);
   p.n = shard_numel;
   p.n_shards = n_shards;
-  p.partials = workspace;
+  p.partials = partials;
   p.out = norm_sq_out;
   p.coef = clip_coef_out;
   p.max_norm = max_norm;
@@ -231,7 +246,15 @@ int zero_grad_norm_sq(const float* const* shards, int n_shards, int64_t shard_nu
     vec = vec && aligned16(shards[k]);
   }
   set_path(vec);
-  return hip_status(launch_norm(p, vec, static_cast<hipStream_t>(stream)), "zero_grad_norm_sq");
+  return hip_status(launch_norm(p, vec, static_cast<hipStream_t>(stream)), where);
+}
+
+int zero_grad_norm_sq(const float* const* shards, int n_shards, int64_t shard_numel,
+                      double* workspace, int64_t workspace_len, double* norm_sq_out,
+                      float max_norm, float* clip_coef_out, void* stream) {
+  TraceRange tr("zero_grad_norm_sq");
+  return norm_common(shards, n_shards, shard_numel, workspace, workspace_len, norm_sq_out, max_norm,
+                     clip_coef_out, stream, "zero_grad_norm_sq");
 }
 
 int zero_grad_norm_sq_no_alloc(const float* const* shards, int n_shards, int64_t shard_numel,
@@ -244,25 +267,8 @@ int zero_grad_norm_sq_no_alloc(const float* const* shards, int n_shards, int64_t
   if (n_shards >= 1 && n_shards <= ZERO_MAX_RANKS &&
       static_cast<int64_t>(n_shards) * ZERO_NORM_BLOCKS > kNormScratchDoubles)
     return fail(ZERO_ERR_SIZE, "grad_norm_no_alloc: the partial sums exceed the library's array");
-  Err e;
-  st = check_grad_norm(shards, n_shards, shard_numel, scratch_dev, kNormScratchDoubles, norm_sq_out,
-                       max_norm, clip_coef_out, e);
-  if (st) return fail(st, e.msg);
-  NormParams p;
-  memset(&p, 0, sizeof p);
-  p.n = shard_numel;
-  p.n_shards = n_shards;
-  p.partials = scratch_dev;
-  p.out = norm_sq_out;
-  p.coef = clip_coef_out;
-  p.max_norm = max_norm;
-  bool vec = true;
-  for (int k = 0; k < n_shards; ++k) {
-    p.x[k] = shards[k];
-    vec = vec && aligned16(shards[k]);
-  }
-  set_path(vec);
-  return hip_status(launch_norm(p, vec, static_cast<hipStream_t>(stream)), "zero_grad_norm_sq_no_alloc");
+  return norm_common(shards, n_shards, shard_numel, scratch_dev, kNormScratchDoubles, norm_sq_out, max_norm,
+                     clip_coef_out, stream, "zero_grad_norm_sq_no_alloc");
 }
 
 int zero_adam_shard_step_dev(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* bf16_out,
@@ -272,25 +278,10 @@ int zero_adam_shard_step_dev(float* master, float* exp_avg, float* exp_avg_sq, u
   Err e;
   int st = check_adam_dev(master, exp_avg, exp_avg_sq, bf16_out, grad, n, scalars_dev, e);
   if (st) return fail(st, e.msg);
-  if (n == 0) return ZERO_OK;
-  if (grad_scale) {
-    st = check_adam_scale(grad_scale, master, exp_avg, exp_avg_sq, bf16_out, n, e);
-    if (st) return fail(st, e.msg);
-  }
-  AdamParams a;
-  memset(&a, 0, sizeof a);
-  a.p = master;
-  a.m = exp_avg;
-  a.v = exp_avg_sq;
-  a.b = bf16_out;
-  a.g = grad;
-  a.gscale = grad_scale;
-  a.n = n;
-  a.sdev = scalars_dev;
-  const bool vec = aligned16(master) && aligned16(exp_avg) && aligned16(exp_avg_sq) &&
-                   aligned16(grad) && aligned8(bf16_out);
-  set_path(vec);
-  return hip_status(launch_adam(a, vec, static_cast<hipStream_t>(stream)), "zero_adam_shard_step_dev");
+  zero_adam_scalars unused;
+  memset(&unused, 0, sizeof unused);
+  return adam_checked(master, exp_avg, exp_avg_sq, bf16_out, grad, grad_scale, n, unused, scalars_dev, stream,
+                      "zero_adam_shard_step_dev");
 }
 
 static int fused_common(const uint16_t* const* rank_grads, const float* rank_weights, int n_ranks,
