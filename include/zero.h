@@ -238,10 +238,12 @@ int zero_reduce_scatter_adam(const uint16_t* const* rank_grads, const float* ran
  * m/v with the combined gradient; [blog] 三级分片, ZeRO-1: the step between
  * the reduce-scatter and the all-gather) and the same arithmetic, with the
  * step's scalars read from device memory when the kernel runs instead of
- * being passed by value at the call.  A caller that captures
- * a step into a HIP graph writes each step's scalars (zero_adam_scalars_compute
- * on the host, then a copy to the device struct on the replay stream) before
- * each replay; the captured launches then apply that step's bias corrections.
+ * being passed by value at the call.  A caller that captures a step into a
+ * HIP graph puts each step's scalars (zero_adam_scalars_compute on the host)
+ * into the device struct before the update kernels of each replay run: with a
+ * copy on the replay stream, or with zero_adam_scalars_fetch captured as the
+ * graph's first kernel; the captured launches then apply that step's bias
+ * corrections.
  * The decay term is applied when the device struct's weight_decay is non-zero,
  * exactly as the host-scalar forms decide it, so results are bit-identical to
  * zero_adam_shard_step / zero_adam_shard_step_scaled / zero_reduce_scatter_adam
@@ -341,6 +343,10 @@ int zero_all_gather_layer(const void* const* shards, int n_shards, int64_t shard
  *   micro-batches 0..mb-1 only.
  * zero_offload_sync: waits for every queued copy and kernel of the handle; the
  *   host shard may be read after it returns.
+ * zero_offload_destroy: waits for the handle's copies and kernels, then frees
+ *   its streams, events and the handle itself (never the caller's buffers);
+ *   NULL is a no-op.  Returns ZERO_ERR_HIP if a wait failed (the handle is
+ *   freed all the same).
  * compute_stream may change from one call to the next: the handle orders its
  * own copies and kernels on each slot by events.  Ordering the writes into
  * slot_contrib after the kernel that last read that slot stays the caller's
