@@ -379,7 +379,7 @@ __global__ __launch_bounds__(kBlock) void norm_partial_kernel(NormParams p) {
 // process ends.  Host code never uses this name as an address: it is a
 // host-side stand-in for the symbol, and the device address comes from
 // norm_scratch_device_ptr.
-static __device__ __align__(256) double norm_scratch[kNormScratchDoubles];
+static __device__ __align__(256) double scratch[kNormScratchDoubles];
 
 __global__ __launch_bounds__(kBlock) void norm_final_kernel(NormParams p) {
   const int64_t total = static_cast<int64_t>(p.n_shards) * p.gx;
@@ -800,7 +800,7 @@ hipError_t norm_scratch_device_ptr(double** out) {
     if (!p) {
       void* addr = nullptr;
       // with `dev` current: this device's copy of the array
-      err = hipGetSymbolAddress(&addr, HIP_SYMBOL(norm_scratch));
+      err = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
       if (err != hipSuccess) return err;
       if (!addr) return hipErrorInvalidSymbol;
       p = static_cast<double*>(addr);
