@@ -21,7 +21,7 @@ np.float32 scalars; there is no fused multiply-add in numpy, and np.sqrt and
 np.divide are correctly rounded).  Dtypes are asserted so that numpy's scalar
 promotion can never silently widen a step to float64.
 
-Readings of points the pages leave open (each is listed in the design notes):
+Readings of points the pages leave open:
 Adam is Kingma & Ba's bias-corrected form with eps outside the square root;
 weight decay is decoupled and scaled by the learning rate; the reduction is
 w_0*x_0 + w_1*x_1 + ... summed left to right in rank order with every product
